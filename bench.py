@@ -1,0 +1,350 @@
+#!/usr/bin/env python3
+"""Throughput of the chunked gated delta rule (forward + backward) on one
+MI355X, through libgdr's C ABI.
+
+One step = gdr_chunk_fwd (saving the per-chunk state snapshots) followed by
+gdr_chunk_bwd on one batch of the fixed-length bf16 workload B=2, T=4096,
+H=16, DK=DV=128 (seeded synthetic inputs, resident in HBM before the timed
+region).  Prints ONE JSON line.  Per-kernel durations come from HIP events
+that libgdr records around each launch on the call's stream (opt-in
+diagnostic timers); the dominant kernel's roofline uses the algorithmic
+byte / flop model of each kernel stated below.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_FLOPS = 2.5e15      # MI355X dense bf16 MFMA
+PEAK_FP32_FLOPS = 157.3e12    # MI355X fp32 matrix
+PEAK_HBM = 8.0e12             # MI355X HBM3E bytes/s
+CH = 64
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target wall time of the oracle sample")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# FLOP formula of the chunked algorithm (per token per head; 2mnk per GEMM,
+# C^3/3 for the triangular inverse, elementwise work not counted)
+
+def flops_fwd(K, V, C=CH):
+    return 6 * K * V + 6 * C * K + 4 * C * V + C * C / 3.0
+
+
+def flops_bwd(K, V, C=CH):
+    return 14 * K * V + 18 * C * K + 10 * C * V + 13 * C * C / 3.0
+
+
+# Algorithmic work of each kernel for one call: bytes of every tensor the
+# kernel reads or writes, counted once, and the flops of the GEMMs it
+# performs (2mnk), for NC chunk-heads, NP (sequence, head) pairs and NT
+# token-heads.  e = io element size, hs = snapshot element size.
+
+def kernel_model(name, mode, NC, NP, NT, K, V, e, hs, C=CH):
+    if name == "wy":
+        rd = NT * (K * e + V * e + 8)
+        wr = NC * (C * 4 + C * K * e + K * C * e + V * C * e)
+        fl = NC * (2 * C * C * K + C ** 3 / 3.0 + 2 * C * C * K + 2 * C * C * V)
+        if mode == "bwd":
+            rd += NT * K * e
+            wr += NC * (C * C * 4 + K * C * e + C * C * e + K * C * e)
+            fl += NC * 2 * C * C * K
+        return rd + wr, fl
+    if name == "scan_fwd":
+        rd = NC * (2 * C * K * e + V * C * e + 4) + NP * K * V * 4
+        wr = NC * (K * V * hs + (V * C * e if mode == "fwd" else 0)) + NP * K * V * 4
+        return rd + wr, NC * 4 * C * K * V
+    if name == "out":
+        rd = NT * 2 * K * e + NC * (K * V * hs + V * C * e + C * 4)
+        wr = NT * V * e
+        return rd + wr, NC * (2 * C * C * K + 2 * C * K * V + 2 * C * C * V)
+    if name == "scan_bwd":
+        rd = NT * (K * e + V * e) + NC * (C * C * e + 2 * K * C * e + 4) + NP * K * V * 4
+        wr = NC * (K * V * e + C * V * e) + NP * K * V * 4
+        return rd + wr, NC * (6 * C * K * V + 2 * C * C * V)
+    if name == "grad":
+        rd = NT * (2 * K * e + 2 * V * e + 4) + NC * (C * 4 + C * K * e + V * C * e + C * C * 4
+                                                      + K * V * hs + K * V * e + C * V * e)
+        wr = NT * (2 * K * e + V * e + 8)
+        fl = NC * (8 * C * K * V + 6 * C * C * V + 14 * C * C * K + 4 * C ** 3)
+        return rd + wr, fl
+    if name == "plan":
+        return 0, 0
+    raise KeyError(name)
+
+
+# ---------------------------------------------------------------------------
+class Hip:
+    """Minimal HIP runtime access for events (ctypes on libamdhip64)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        rc = self.lib.hipEventCreate(ctypes.byref(e))
+        if rc != 0:
+            raise RuntimeError("hipEventCreate failed: %d" % rc)
+        return e.value
+
+    def record(self, ev, stream):
+        rc = self.lib.hipEventRecord(ev, stream)
+        if rc != 0:
+            raise RuntimeError("hipEventRecord failed: %d" % rc)
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed: %d" % rc)
+        return float(ms.value)
+
+    def destroy(self, ev):
+        self.lib.hipEventDestroy(ev)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "chunked_gated_delta_02_amd", "csrc"))):
+        with open(os.path.join(ROOT, "chunked_gated_delta_02_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 --pmc summaries, if they
+    were taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "%s_%s_pmc.json" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+def cpu_baseline(w, inp, target_s):
+    """The oracle (fp64, OpenMP over (sequence, head)) on a bounded sample of
+    the workload: all sequences, a subset of heads sized to ~target_s."""
+    import numpy as np
+    from oracle import oracle
+    threads = oracle.max_threads()
+    H = w.H
+
+    def run(nh):
+        sel = lambda t: t[:, :, :nh].double().numpy()
+        q, k, v, beta, g, do = (sel(inp[n]) for n in ("q", "k", "v", "beta", "g", "do"))
+        dhT = None if inp["dhT"] is None else inp["dhT"][:, :nh].double().numpy()
+        t0 = time.perf_counter()
+        oracle.fwd(q, k, v, beta, g, layout=w.layout)
+        oracle.bwd(q, k, v, beta, g, do, dhT=dhT, layout=w.layout)
+        return time.perf_counter() - t0
+
+    # calibrate with as many heads as threads can take in one wave of pairs,
+    # then grow the head subset (and, if the whole workload is quicker than
+    # the target, repeat it) until the sample holds ~target_s of CPU work
+    nh = max(1, min(H, threads // max(1, w.B)))
+    t = run(nh)
+    pairs_per_s = nh * w.B / t
+    want = int(pairs_per_s * target_s / w.B)
+    nh2 = max(1, min(H, want))
+    reps = 1
+    if nh2 > nh:
+        nh, t = nh2, run(nh2)
+    if nh == H and t < target_s / 2:
+        reps = max(1, int(target_s / t))
+        t = sum(run(nh) for _ in range(reps))
+    tokens = reps * w.B * w.T * nh / H
+    return {"value": tokens / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "fp64 oracle forward+backward on %d of %d heads of all %d sequences "
+                      "(%d tokens x %d heads), %d repetition(s), %.1f s wall; tokens/s counts "
+                      "full tokens (all heads)" % (nh, H, w.B, w.B * w.T, nh, reps, t)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(asked for --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from chunked_gated_delta_02_amd import _lib, inputs as gin, ops
+
+    w = gin.CONFIGS[args.config]
+    if w.cp_segments != 1:
+        w = w.replace(cp_segments=1)
+    inp = gin.generate(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    q, k, v, beta, g, do = (d[n] for n in ("q", "k", "v", "beta", "g", "do"))
+    h0, dhT, cu = d["h0"], d["dhT"], d["cu_seqlens"]
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    N = inp["N"]
+    p = ops.make_problem(q, v, cu, w.layout, None, w.h_store)
+    st = _lib.gdr_check(p)
+    if st != _lib.GDR_OK:
+        raise _lib.GDRError(st, _lib.last_error())
+    sshape = (N, H, K, V) if w.layout == "KV" else (N, H, V, K)
+    o = torch.empty_like(v)
+    hT = torch.empty(sshape, dtype=torch.float32, device=dev)
+    hs_dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.h_store]
+    h_saved = torch.empty(_lib.gdr_h_saved_bytes(p) // hs_dt.itemsize, dtype=hs_dt, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dbeta, dg = torch.empty_like(beta), torch.empty_like(g)
+    dh0 = torch.empty(sshape, dtype=torch.float32, device=dev)
+    fws = _lib.gdr_fwd_workspace_bytes(p)
+    bws = _lib.gdr_bwd_workspace_bytes(p, True)
+    wsf = torch.empty(fws, dtype=torch.uint8, device=dev)
+    wsb = torch.empty(bws, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    P = lambda t: 0 if t is None else t.data_ptr()
+
+    def fwd():
+        _lib.gdr_chunk_fwd(p, P(q), P(k), P(v), P(beta), P(g), P(cu), P(h0), P(o), P(hT), P(h_saved),
+                           P(wsf), fws, stream)
+
+    def bwd():
+        _lib.gdr_chunk_bwd(p, P(q), P(k), P(v), P(beta), P(g), P(cu), P(h0), P(h_saved), P(do), P(dhT),
+                           P(dq), P(dk), P(dv), P(dbeta), P(dg), P(dh0), P(wsb), bws, stream)
+
+    hip = Hip()
+    nk = len(_lib.KERNELS)
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+
+    # timed region: K steps; libgdr records per-kernel events for each call
+    evs = [[[hip.event() for _ in range(2 * nk)] for _ in range(2)] for _ in range(args.steps)]
+    e0, e1 = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    t_host0 = time.perf_counter()
+    hip.record(e0, stream)
+    for s in range(args.steps):
+        _lib.gdr_set_kernel_timers(evs[s][0])
+        fwd()
+        _lib.gdr_set_kernel_timers(evs[s][1])
+        bwd()
+    _lib.gdr_set_kernel_timers(None)
+    hip.record(e1, stream)
+    torch.cuda.synchronize()
+    t_host1 = time.perf_counter()
+    total_ms = hip.elapsed_ms(e0, e1)
+    ms_step = total_ms / args.steps
+
+    # per-kernel averages
+    per = {}
+    for phase_i, phase in enumerate(("fwd", "bwd")):
+        for ki, kname in enumerate(_lib.KERNELS):
+            times = []
+            for s in range(args.steps):
+                a, b = evs[s][phase_i][2 * ki], evs[s][phase_i][2 * ki + 1]
+                try:
+                    times.append(hip.elapsed_ms(a, b))
+                except RuntimeError:
+                    break  # kernel not launched in this phase
+            if len(times) == args.steps:
+                per["%s.%s" % (phase, kname)] = sum(times) / len(times)
+    for row in evs:
+        for ph in row:
+            for e in ph:
+                hip.destroy(e)
+
+    tokens = B * T
+    NT = B * T * H
+    NC = B * ((T + CH - 1) // CH) * H if cu is None else None
+    NP = N * H
+    e = q.element_size()
+    hs = hs_dt.itemsize
+    fl_f = NT * flops_fwd(K, V)
+    fl_b = NT * flops_bwd(K, V)
+    peak = PEAK_BF16_FLOPS if q.dtype == torch.bfloat16 else PEAK_FP32_FLOPS
+
+    kernels = {}
+    for key, ms in per.items():
+        phase, kname = key.split(".")
+        byt, fl = kernel_model(kname, phase, NC, NP, NT, K, V, e, hs)
+        kernels[key] = {"avg_us": round(ms * 1e3, 2), "GBps": round(byt / (ms * 1e-3) / 1e9, 1),
+                        "TFLOPs": round(fl / (ms * 1e-3) / 1e12, 2)}
+    dom = max(per, key=per.get)
+    phase, kname = dom.split(".")
+    byt, fl = kernel_model(kname, phase, NC, NP, NT, K, V, e, hs)
+    t_dom = per[dom] * 1e-3
+    if byt / PEAK_HBM >= fl / peak:
+        roof = {"bound": "hbm", "achieved": round(byt / t_dom / 1e9, 1), "peak": PEAK_HBM / 1e9,
+                "unit": "GB/s", "frac": round(byt / t_dom / PEAK_HBM, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(fl / t_dom / 1e12, 2), "peak": peak / 1e12,
+                "unit": "TFLOP/s", "frac": round(fl / t_dom / peak, 4)}
+    roof["kernel"] = "k_%s (%s)" % (kname, phase)
+    roof["avg_us"] = round(per[dom] * 1e3, 2)
+    roof["algorithmic_bytes"] = int(byt)
+    roof["algorithmic_flops"] = int(fl)
+    roof["traffic"] = measured_traffic(kname + "_" + phase, w.name)
+
+    fwd_ms = sum(v for k2, v in per.items() if k2.startswith("fwd."))
+    bwd_ms = sum(v for k2, v in per.items() if k2.startswith("bwd."))
+    res = {
+        "metric": "GDR fwd+bwd tokens/s & TFLOPS (% bf16 MFMA peak), B=2 T=4096 H=16 D=128",
+        "value": round(tokens / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if q.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "T": T, "H": H, "DK": K, "DV": V, "chunk": CH,
+                   "layout": w.layout, "h_store": w.h_store, "seed": w.seed,
+                   "parallelism": "single GPU"},
+        "tflops": {"fwd+bwd": round((fl_f + fl_b) / (ms_step * 1e-3) / 1e12, 2),
+                   "fwd_kernels": round(fl_f / (fwd_ms * 1e-3) / 1e12, 2) if fwd_ms else None,
+                   "bwd_kernels": round(fl_b / (bwd_ms * 1e-3) / 1e12, 2) if bwd_ms else None},
+        "frac_bf16_peak": round((fl_f + fl_b) / (ms_step * 1e-3) / PEAK_BF16_FLOPS, 4),
+        "fwd_ms": round(fwd_ms, 4),
+        "bwd_ms": round(bwd_ms, 4),
+        "host_wall_ms_per_step": round((t_host1 - t_host0) * 1e3 / args.steps, 4),
+        "kernels": kernels,
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,152 @@
+"""ctypes binding of libgdr's C ABI (include/libgdr.h), same names.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libgdr.so.  Loading fails loudly if the library has not been
+built -- there is no fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgdr.so")
+
+GDR_OK, GDR_ERR_INVALID_ARG, GDR_ERR_UNSUPPORTED, GDR_ERR_WORKSPACE, GDR_ERR_HIP = range(5)
+GDR_F32, GDR_BF16, GDR_F16 = 0, 1, 2
+GDR_LAYOUT_KV, GDR_LAYOUT_VK = 0, 1
+
+# every function the header declares, for the export check
+EXPORTS = ("gdr_check", "gdr_fwd_workspace_bytes", "gdr_bwd_workspace_bytes", "gdr_h_saved_bytes",
+           "gdr_chunk_fwd", "gdr_chunk_bwd", "gdr_set_kernel_timers", "gdr_status_string",
+           "gdr_last_error", "gdr_version")
+KERNELS = ("plan", "wy", "scan_fwd", "out", "scan_bwd", "grad")
+
+
+class gdr_problem(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("seqlen", ctypes.c_int32),
+        ("num_seqs", ctypes.c_int32),
+        ("varlen", ctypes.c_int32),
+        ("heads", ctypes.c_int32),
+        ("dk", ctypes.c_int32),
+        ("dv", ctypes.c_int32),
+        ("chunk", ctypes.c_int32),
+        ("io_dtype", ctypes.c_int32),
+        ("h_store_dtype", ctypes.c_int32),
+        ("layout", ctypes.c_int32),
+        ("cp_segments", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+    ]
+
+
+class GDRError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s: %s" % (status_string(status), message))
+        self.status = status
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libgdr.so; raises if it is missing (build it first)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError(
+                "libgdr.so is not built (%s). Build it with "
+                "`python -c 'import __graft_entry__ as g; g.build()'` or "
+                "`python chunked_gated_delta_02_amd/build.py`." % path)
+        lib = ctypes.CDLL(path)
+        P = ctypes.POINTER(gdr_problem)
+        vp, fp, ip = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
+        lib.gdr_check.argtypes = [P]
+        lib.gdr_check.restype = ctypes.c_int
+        lib.gdr_fwd_workspace_bytes.argtypes = [P]
+        lib.gdr_fwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.gdr_bwd_workspace_bytes.argtypes = [P, ctypes.c_int]
+        lib.gdr_bwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.gdr_h_saved_bytes.argtypes = [P]
+        lib.gdr_h_saved_bytes.restype = ctypes.c_size_t
+        lib.gdr_chunk_fwd.argtypes = [P, vp, vp, vp, fp, fp, ip, fp, vp, fp, vp, vp, ctypes.c_size_t, vp]
+        lib.gdr_chunk_fwd.restype = ctypes.c_int
+        lib.gdr_chunk_bwd.argtypes = [P, vp, vp, vp, fp, fp, ip, fp, vp, vp, fp, vp, vp, vp, fp, fp, fp,
+                                      vp, ctypes.c_size_t, vp]
+        lib.gdr_chunk_bwd.restype = ctypes.c_int
+        lib.gdr_set_kernel_timers.argtypes = [ctypes.c_void_p]
+        lib.gdr_set_kernel_timers.restype = ctypes.c_int
+        lib.gdr_status_string.argtypes = [ctypes.c_int]
+        lib.gdr_status_string.restype = ctypes.c_char_p
+        lib.gdr_last_error.argtypes = []
+        lib.gdr_last_error.restype = ctypes.c_char_p
+        lib.gdr_version.argtypes = []
+        lib.gdr_version.restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def status_string(status: int) -> str:
+    return load().gdr_status_string(int(status)).decode()
+
+
+def last_error() -> str:
+    return load().gdr_last_error().decode()
+
+
+def _raise_on(status: int) -> int:
+    if status != GDR_OK:
+        raise GDRError(status, last_error())
+    return status
+
+
+def gdr_check(p: gdr_problem) -> int:
+    return load().gdr_check(ctypes.byref(p))
+
+
+def gdr_fwd_workspace_bytes(p: gdr_problem) -> int:
+    return load().gdr_fwd_workspace_bytes(ctypes.byref(p))
+
+
+def gdr_bwd_workspace_bytes(p: gdr_problem, have_h_saved: bool) -> int:
+    return load().gdr_bwd_workspace_bytes(ctypes.byref(p), int(bool(have_h_saved)))
+
+
+def gdr_h_saved_bytes(p: gdr_problem) -> int:
+    return load().gdr_h_saved_bytes(ctypes.byref(p))
+
+
+def gdr_version() -> int:
+    return load().gdr_version()
+
+
+def gdr_chunk_fwd(p, q, k, v, beta, g, cu_seqlens, h0, o, hT, h_saved, ws, ws_bytes, stream,
+                  check=True) -> int:
+    """Raw call; all tensor arguments are integer device addresses (0 = NULL)."""
+    st = load().gdr_chunk_fwd(ctypes.byref(p), q, k, v, beta, g, cu_seqlens or None, h0 or None, o,
+                              hT or None, h_saved or None, ws or None, ws_bytes, stream or None)
+    return _raise_on(st) if check else st
+
+
+def gdr_chunk_bwd(p, q, k, v, beta, g, cu_seqlens, h0, h_saved, dO, dhT, dq, dk, dv, dbeta, dg,
+                  dh0, ws, ws_bytes, stream, check=True) -> int:
+    """Raw call; all tensor arguments are integer device addresses (0 = NULL)."""
+    st = load().gdr_chunk_bwd(ctypes.byref(p), q, k, v, beta, g, cu_seqlens or None, h0 or None,
+                              h_saved or None, dO, dhT or None, dq, dk, dv, dbeta, dg, dh0 or None,
+                              ws or None, ws_bytes, stream or None)
+    return _raise_on(st) if check else st
+
+
+def gdr_set_kernel_timers(events) -> int:
+    """events: None, or a sequence of 2 * len(KERNELS) hipEvent_t handles
+    (ints, 0 = not timed) -- (start, stop) per kernel id."""
+    if events is None:
+        return _raise_on(load().gdr_set_kernel_timers(None))
+    assert len(events) == 2 * len(KERNELS)
+    arr = (ctypes.c_void_p * len(events))(*[e or None for e in events])
+    return _raise_on(load().gdr_set_kernel_timers(arr))

@@ -1,0 +1,654 @@
+// gdr_bwd.hip -- backward kernels of the chunked gated delta rule on gfx950
+// (the fused backward that FlashQLA PR #34, "SM120/121 : Add support for
+// fused backward kernel", section "Summary", calls fused_gdr_bwd).
+//
+// Reverse-mode differentiation of the chunk-wise forward (see gdr_fwd.hip),
+// per chunk with state h at its start, dh = gradient of the state at its end
+// and dO, all in KV form:
+//   dDelta  = scale P^T dO + Kt dh                    (P = Q K^T * Gam)
+//   dh_prev = scale Qg^T dO + e^{gamma_L} dh - W^T dDelta    (Qg = e^gamma Q)
+//   dq  = e^gamma (scale dO h^T) + (dP * Gam) K,      dP = scale dO Delta^T
+//   dk  = E (Delta dh^T) + (dP * Gam)^T Q + beta e^gamma (T^T dW)
+//         + G K + G^T K,        E = e^{gamma_L - gamma}, dW = -dDelta h^T,
+//                               G = dA * beta Gam (strictly lower)
+//   dv  = beta (T^T dDelta)
+//   dA  = strictly_lower(-T^T dT T^T),  dT = dDelta (beta V)^T + dW (beta e^gamma K)^T
+//   dbeta = rowsum(V * T^T dDelta) + e^gamma rowsum(K * T^T dW) + rowsum(dA * K K^T * Gam)
+//   dgamma collects e^gamma rowsum(Q * scale dO h^T), rowsum - colsum of
+//   dP * P and dA * A, -rowsum(K * E Delta dh^T) (plus its sum into gamma_L),
+//   beta e^gamma rowsum(K * T^T dW) and e^{gamma_L} <dh, h> into gamma_L;
+//   dg is the chunk-local reverse cumulative sum of dgamma.
+// Sums across tiles run in a fixed order (no floating-point atomics), so
+// results are bitwise reproducible -- the determinism requirement argued in
+// Dao-AILab/quack PR #101 ("Rmsnorm backward fusing sum", review thread).
+//
+// Kernels:
+//   k_scan_bwd  serial over chunks (last to first) per (sequence, head, DV
+//               tile): dh lives in fp32 MFMA accumulators; writes the per-chunk
+//               dh snapshot, dDelta and dh0.
+//   k_grad      chunk-parallel: every intra-chunk gradient GEMM, the WY/UT
+//               backward and the dbeta / dg reductions, in one kernel.
+#include "gdr_kernels.h"
+
+namespace gdr {
+
+// ---------------------------------------------------------------------------
+template <typename T, int DK, int DVT>
+__global__ __launch_bounds__(256) void k_scan_bwd(const ScanBwdArgs a) {
+  constexpr int P = pad_of<T>();
+  constexpr int LDH = DK + P;
+  constexpr int LDD = 64 + P;
+  constexpr int LDO = DVT + P;
+  constexpr int KW = Mma<T>::KW;
+  constexpr int MTH = DK / 64;
+  constexpr int NT = DVT / 16;
+  __shared__ __align__(16) T sDH[DVT * LDH];  // dh^T (dv, dk), operand copy
+  __shared__ __align__(16) T sDO[64 * LDO];   // dO rows (r, dv)
+  __shared__ __align__(16) T sDD[DVT * LDD];  // dDelta^T (dv, r)
+
+  const int H = a.geo.H, DV = a.DV;
+  const int Pn = a.geo.N * H;
+  const int b = blockIdx.x;
+  const int jt = b / Pn, p = b - jt * Pn;
+  const int n = p / H, h = p - n * H;
+  const int dv0 = jt * DVT;
+  int c0, nc, ts, tl;
+  seq_range(a.geo, n, c0, nc, ts, tl);
+  const int w = wave_id();
+  const int dkw = w * (DK / 4);
+  const T* kp = (const T*)a.k;
+  const T* dop = (const T*)a.dO;
+
+  f32x4 acc_h[MTH][NT];
+  const int64_t sb = (int64_t)(n * H + h) * DK * DV;
+#pragma unroll
+  for (int mt = 0; mt < MTH; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int dk = dkw + 16 * mt + acc_row0() + i, dv = dv0 + 16 * nt + acc_col();
+        float v = 0.f;
+        if (a.dhT) v = (a.layout == 0) ? a.dhT[sb + (int64_t)dk * DV + dv] : a.dhT[sb + (int64_t)dv * DK + dk];
+        acc_h[mt][nt][i] = v;
+      }
+#pragma unroll
+  for (int mt = 0; mt < MTH; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) store_acc_t(sDH, LDH, dkw + 16 * mt, 16 * nt, acc_h[mt][nt]);
+
+  for (int c = nc - 1; c >= 0; --c) {
+    const int ci = c0 + c;
+    const int64_t ch = (int64_t)ci * H + h;
+    const int t0 = ts + c * CH;
+    const int len = min(CH, tl - c * CH);
+    {
+      T* db = (T*)a.dhs + ch * DK * DV + dv0;
+#pragma unroll
+      for (int mt = 0; mt < MTH; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) store_acc(db, DV, dkw + 16 * mt, 16 * nt, acc_h[mt][nt]);
+    }
+    __syncthreads();  // previous chunk's readers of sDO / sDD are done
+    load_rows<T, DVT>(sDO, LDO, dop + ((int64_t)t0 * H + h) * DV + dv0, (int64_t)H * DV, len);
+    __syncthreads();
+    const float gL = a.gam[ch * 64 + 63];
+    // dDelta = E (K dh) + scale P^T dO, rows 16w
+    f32x4 acc_d[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc_d[nt] = zero4();
+    const T* kb = kp + ((int64_t)t0 * H + h) * DK;
+#pragma unroll
+    for (int ks = 0; ks < DK; ks += KW) {
+      const auto af = frag_rowk_masked(kb, (int64_t)H * DK, 16 * w, ks, len);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc_d[nt] = Mma<T>::mma(af, frag_rowk(sDH, LDH, 16 * nt, ks), acc_d[nt]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float E = expf(gL - a.gam[ch * 64 + 16 * w + acc_row0() + i]);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc_d[nt][i] *= E;
+    }
+    const T* Pb = (const T*)a.PsT + ch * 4096;
+#pragma unroll
+    for (int ks = 0; ks < 64; ks += KW) {
+      const auto af = frag_rowk(Pb, 64, 16 * w, ks);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc_d[nt] = Mma<T>::mma(af, frag_colk_lds(sDO, LDO, 16 * nt, ks), acc_d[nt]);
+    }
+    {
+      T* ddb = (T*)a.dD + ch * 64 * DV + dv0;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        store_acc_t(sDD, LDD, 16 * w, 16 * nt, acc_d[nt]);
+        store_acc(ddb, DV, 16 * w, 16 * nt, acc_d[nt]);
+      }
+    }
+    __syncthreads();
+    // dh <- e^{gamma_L} dh + (scale Qg)^T dO - W^T dDelta
+    const float eL = expf(gL);
+#pragma unroll
+    for (int mt = 0; mt < MTH; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc_h[mt][nt] *= eL;
+    const T* Qb = (const T*)a.QgsT + ch * DK * 64;
+    const T* Wb = (const T*)a.WT + ch * DK * 64;
+#pragma unroll
+    for (int ks = 0; ks < 64; ks += KW) {
+      typename Mma<T>::frag aq[MTH], aw[MTH];
+#pragma unroll
+      for (int mt = 0; mt < MTH; ++mt) {
+        aq[mt] = frag_rowk(Qb, 64, dkw + 16 * mt, ks);
+        aw[mt] = Mma<T>::neg(frag_rowk(Wb, 64, dkw + 16 * mt, ks));
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const auto bo = frag_colk_lds(sDO, LDO, 16 * nt, ks);
+        const auto bd = frag_rowk(sDD, LDD, 16 * nt, ks);
+#pragma unroll
+        for (int mt = 0; mt < MTH; ++mt) {
+          acc_h[mt][nt] = Mma<T>::mma(aq[mt], bo, acc_h[mt][nt]);
+          acc_h[mt][nt] = Mma<T>::mma(aw[mt], bd, acc_h[mt][nt]);
+        }
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < MTH; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) store_acc_t(sDH, LDH, dkw + 16 * mt, 16 * nt, acc_h[mt][nt]);
+  }
+  if (a.dh0) {
+#pragma unroll
+    for (int mt = 0; mt < MTH; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int dk = dkw + 16 * mt + acc_row0() + i, dv = dv0 + 16 * nt + acc_col();
+          if (a.layout == 0) a.dh0[sb + (int64_t)dk * DV + dv] = acc_h[mt][nt][i];
+          else a.dh0[sb + (int64_t)dv * DK + dk] = acc_h[mt][nt][i];
+        }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// k_grad: per (chunk, head).  Phase 1 loops over DV in blocks of DVB and
+// accumulates the DV-contracted products (dQg, dKt, dW, dP, dT_V) in
+// registers while emitting dv; phase 2 finishes dq, dk, dbeta and dg.  Wave
+// w owns output rows 16w..16w+15 of every 64-row product, so all row sums
+// stay inside one wavefront; column sums go through per-wave LDS partials
+// reduced in a fixed order.
+template <typename T, typename HS, int DK>
+__global__ __launch_bounds__(256) void k_grad(const GradArgs a) {
+  constexpr int P = pad_of<T>();
+  constexpr int LDK = DK + P;
+  constexpr int L64 = 64 + P;
+  constexpr int DVB = dvb_of<T>();
+  constexpr int LDV = DVB + P;
+  constexpr int KW = Mma<T>::KW;
+  constexpr int NTK = DK / 16;
+  constexpr int NTB = DVB / 16;
+  typedef typename Mma<T>::frag frag;
+  constexpr int PH1 = (DVB * LDK + DK * LDV + DVB * L64 + 2 * 64 * LDV) * (int)sizeof(T);
+  constexpr int PH2 = (2 * 64 * LDK + DK * L64 + 64 * L64) * (int)sizeof(T);
+  extern __shared__ __align__(16) char smem[];
+  T* sT = (T*)smem;                       // T (r, s), operand copy
+  float* sg = (float*)(sT + 64 * L64);    // gamma
+  float* sb = sg + 64;                    // beta
+  float* seg = sb + 64;                   // e^gamma
+  float* sE = seg + 64;                   // e^{gamma_L - gamma}
+  float* sRed = sE + 64;                  // [2][4][64] column-sum partials
+  float* sMisc = sRed + 2 * 4 * 64;       // [8]: per-wave gamma_L partials
+  char* uni = (char*)(sMisc + 8);
+  // phase 1
+  T* sHvk = (T*)uni;                      // h rows (dv, dk)
+  T* sDHkv = sHvk + DVB * LDK;            // dh (dk, dv)
+  T* sDeltaT = sDHkv + DK * LDV;          // Delta^T (dv, r)
+  T* sDD = sDeltaT + DVB * L64;           // dDelta (r, dv)
+  T* sV = sDD + 64 * LDV;                 // V (r, dv)
+  // phase 2 (aliases phase 1)
+  T* sQ = (T*)uni;                        // Q (r, dk); later dT^T (s, r)
+  T* sK = sQ + 64 * LDK;                  // K (r, dk)
+  T* sdWT = sK + 64 * LDK;                // dW^T (dk, r); later G^T (c, a)
+  T* sdQKT = sdWT + DK * L64;             // (dP * Gam)^T (s, r); later Y^T (b, a)
+  static_assert(PH1 > 0 && PH2 > 0, "");
+
+  const int ci = blockIdx.x, h = blockIdx.y;
+  int n, t0, len;
+  if (!chunk_lookup(a.geo, ci, n, t0, len)) return;
+  const int H = a.geo.H, DV = a.DV;
+  const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+  const int64_t ch = (int64_t)ci * H + h;
+  const T* qp = (const T*)a.q;
+  const T* kp = (const T*)a.k;
+  const T* vp = (const T*)a.v;
+  const T* dop = (const T*)a.dO;
+  const float scale = a.scale;
+
+  if (tid < 64) {
+    const float gm = a.gam[ch * 64 + tid];
+    const float gL = a.gam[ch * 64 + 63];
+    sg[tid] = gm;
+    sb[tid] = (tid < len) ? a.beta[(int64_t)(t0 + tid) * H + h] : 0.f;
+    seg[tid] = expf(gm);
+    sE[tid] = expf(gL - gm);
+  }
+  for (int e = tid; e < 64 * 64; e += 256) sT[(e >> 6) * L64 + (e & 63)] = from_f32<T>(a.Tm[ch * 4096 + e]);
+  const int rw = 16 * w;            // first output row of this wave
+  const int r0 = rw + acc_row0();   // lane's rows r0..r0+3
+
+  // per-lane row partials for the lane's 4 rows
+  float rg[4] = {0.f, 0.f, 0.f, 0.f};   // dgamma row terms
+  float rb[4] = {0.f, 0.f, 0.f, 0.f};   // dbeta row terms
+  float gLh = 0.f;                      // <dh, h> partial (times e^{gamma_L} later)
+  float gLy = 0.f;                      // sum of E rowsum(K * Delta dh^T) partial
+
+  // W fragments for Delta = U - W h (rows 16w), negated
+  frag wf[DK / KW];
+  {
+    const T* Wb = (const T*)a.W + ch * 64 * DK;
+#pragma unroll
+    for (int ks = 0; ks < DK / KW; ++ks) wf[ks] = Mma<T>::neg(frag_rowk(Wb, DK, rw, ks * KW));
+  }
+  f32x4 aQ[NTK], aKt[NTK], aW[NTK], aP[4], aTV[4];
+#pragma unroll
+  for (int nt = 0; nt < NTK; ++nt) aQ[nt] = aKt[nt] = aW[nt] = zero4();
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) aP[nt] = aTV[nt] = zero4();
+
+  const int64_t rowq = (int64_t)t0 * H + h;   // token-row index of chunk row 0
+  for (int dvb = 0; dvb < DV; dvb += DVB) {
+    __syncthreads();
+    load_rows_conv<HS, T, DK, DVB>(sHvk, LDK, (const HS*)a.hs + (ch * DV + dvb) * DK, DK, DVB);
+    load_rows<T, DVB, DK>(sDHkv, LDV, (const T*)a.dhs + ch * DK * DV + dvb, DV, DK);
+    load_rows<T, DVB>(sDD, LDV, (const T*)a.dD + ch * 64 * DV + dvb, DV, 64);
+    load_rows<T, DVB>(sV, LDV, vp + rowq * DV + dvb, (int64_t)H * DV, len);
+    __syncthreads();
+    // e^{gamma_L} <dh, h>: h from the snapshot in its stored precision
+    {
+      const HS* hb = (const HS*)a.hs + (ch * DV + dvb) * DK;
+      for (int e = tid; e < DVB * DK; e += 256) {
+        const int dvl = e / DK, dk = e - dvl * DK;
+        gLh += to_f32(hb[e]) * to_f32(sDHkv[dk * LDV + dvl]);
+      }
+    }
+    // Delta block = U - W h  (rows 16w)
+    f32x4 aD[NTB];
+    {
+      const T* Ub = (const T*)a.UT + (ch * DV + dvb) * 64;
+#pragma unroll
+      for (int nt = 0; nt < NTB; ++nt) aD[nt] = load4f(Ub + (16 * nt + acc_col()) * 64 + r0);
+#pragma unroll
+      for (int ks = 0; ks < DK / KW; ++ks)
+#pragma unroll
+        for (int nt = 0; nt < NTB; ++nt)
+          aD[nt] = Mma<T>::mma(wf[ks], frag_rowk(sHvk, LDK, 16 * nt, ks * KW), aD[nt]);
+#pragma unroll
+      for (int nt = 0; nt < NTB; ++nt) store_acc_t(sDeltaT, L64, rw, 16 * nt, aD[nt]);
+    }
+    // dO fragments (rows 16w, k = dv)
+    frag dof[DVB / KW];
+#pragma unroll
+    for (int ks = 0; ks < DVB / KW; ++ks)
+      dof[ks] = frag_rowk_masked(dop + rowq * DV + dvb, (int64_t)H * DV, rw, ks * KW, len);
+    // dQg += dO h^T ; dW -= dDelta h^T ; dT_V += dDelta V^T
+#pragma unroll
+    for (int ks = 0; ks < DVB / KW; ++ks) {
+      const frag ddp = frag_rowk(sDD, LDV, rw, ks * KW);
+      const frag ddn = Mma<T>::neg(ddp);
+#pragma unroll
+      for (int nt = 0; nt < NTK; ++nt) {
+        const frag bh = frag_colk_lds(sHvk, LDK, 16 * nt, ks * KW);
+        aQ[nt] = Mma<T>::mma(dof[ks], bh, aQ[nt]);
+        aW[nt] = Mma<T>::mma(ddn, bh, aW[nt]);
+      }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) aTV[nt] = Mma<T>::mma(ddp, frag_rowk(sV, LDV, 16 * nt, ks * KW), aTV[nt]);
+    }
+    __syncthreads();  // Delta^T complete
+    // dKt += Delta dh^T ; dP += dO Delta^T
+#pragma unroll
+    for (int ks = 0; ks < DVB / KW; ++ks) {
+      const frag ad = frag_colk_lds(sDeltaT, L64, rw, ks * KW);
+#pragma unroll
+      for (int nt = 0; nt < NTK; ++nt) aKt[nt] = Mma<T>::mma(ad, frag_rowk(sDHkv, LDV, 16 * nt, ks * KW), aKt[nt]);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) aP[nt] = Mma<T>::mma(dof[ks], frag_colk_lds(sDeltaT, L64, 16 * nt, ks * KW), aP[nt]);
+    }
+    // dVb = T^T dDelta (rows s = 16w): dv = beta dVb, dbeta += rowsum(V dVb)
+    {
+      f32x4 aVb[NTB];
+#pragma unroll
+      for (int nt = 0; nt < NTB; ++nt) aVb[nt] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < 64; ks += KW) {
+        const frag at = frag_colk_lds(sT, L64, rw, ks);
+#pragma unroll
+        for (int nt = 0; nt < NTB; ++nt) aVb[nt] = Mma<T>::mma(at, frag_colk_lds(sDD, LDV, 16 * nt, ks), aVb[nt]);
+      }
+      T* dvp = (T*)a.dv;
+#pragma unroll
+      for (int nt = 0; nt < NTB; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int s = r0 + i, dvl = 16 * nt + acc_col();
+          const float x = aVb[nt][i];
+          rb[i] += to_f32(sV[s * LDV + dvl]) * x;
+          if (s < len) dvp[((int64_t)(t0 + s) * H + h) * DV + dvb + dvl] = from_f32<T>(sb[s] * x);
+        }
+    }
+  }
+
+  // ---------------- phase 2 ----------------
+  __syncthreads();
+  load_rows<T, DK>(sQ, LDK, qp + rowq * DK, (int64_t)H * DK, len);
+  load_rows<T, DK>(sK, LDK, kp + rowq * DK, (int64_t)H * DK, len);
+  // dW^T -> LDS (aW holds dW rows 16w)
+#pragma unroll
+  for (int nt = 0; nt < NTK; ++nt) store_acc_t(sdWT, L64, rw, 16 * nt, aW[nt]);
+  // dP (scaled, masked) and dQK = dP * Gam -> LDS as (dP * Gam)^T
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    f32x4 dq4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = r0 + i, s = 16 * nt + acc_col();
+      const float dp = (s <= r) ? scale * aP[nt][i] : 0.f;
+      aP[nt][i] = dp;
+      dq4[i] = (s <= r) ? dp * expf(sg[r] - sg[s]) : 0.f;
+    }
+    store_acc_t(sdQKT, L64, rw, 16 * nt, dq4);
+  }
+  __syncthreads();
+
+  // dgamma from P: rowsum - colsum of dP * P,  P = Q K^T * Gam
+  {
+    f32x4 aPP[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) aPP[nt] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < DK; ks += KW) {
+      const frag af = frag_rowk(sQ, LDK, rw, ks);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) aPP[nt] = Mma<T>::mma(af, frag_rowk(sK, LDK, 16 * nt, ks), aPP[nt]);
+    }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      float cs = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + i, s = 16 * nt + acc_col();
+        const float x = (s <= r) ? aP[nt][i] * aPP[nt][i] * expf(sg[r] - sg[s]) : 0.f;
+        rg[i] += x;
+        cs += x;
+      }
+      cs = sum4g(cs);
+      if (l < 16) sRed[0 * 256 + w * 64 + 16 * nt + l] = cs;
+    }
+  }
+  // dq = e^gamma (scale dO h^T) + (dP * Gam) K ; dgamma += e^gamma rowsum(Q * scale dO h^T)
+  {
+#pragma unroll
+    for (int nt = 0; nt < NTK; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + i, dk = 16 * nt + acc_col();
+        const float x = scale * aQ[nt][i];
+        rg[i] += seg[r] * x * to_f32(sQ[r * LDK + dk]);
+        aQ[nt][i] = seg[r] * x;
+      }
+#pragma unroll
+    for (int ks = 0; ks < 64; ks += KW) {
+      const frag af = frag_colk_lds(sdQKT, L64, rw, ks);
+#pragma unroll
+      for (int nt = 0; nt < NTK; ++nt) aQ[nt] = Mma<T>::mma(af, frag_colk_lds(sK, LDK, 16 * nt, ks), aQ[nt]);
+    }
+    T* dqp = (T*)a.dq;
+#pragma unroll
+    for (int nt = 0; nt < NTK; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + i;
+        if (r < len) dqp[((int64_t)(t0 + r) * H + h) * DK + 16 * nt + acc_col()] = from_f32<T>(aQ[nt][i]);
+      }
+  }
+  // dk = E (Delta dh^T) + (dP * Gam)^T Q ; dgamma -= y, gamma_L += sum y
+  {
+#pragma unroll
+    for (int nt = 0; nt < NTK; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + i, dk = 16 * nt + acc_col();
+        const float y = sE[r] * aKt[nt][i] * to_f32(sK[r * LDK + dk]);
+        rg[i] -= y;
+        gLy += y;
+        aKt[nt][i] *= sE[r];
+      }
+#pragma unroll
+    for (int ks = 0; ks < 64; ks += KW) {
+      const frag af = frag_rowk(sdQKT, L64, rw, ks);
+#pragma unroll
+      for (int nt = 0; nt < NTK; ++nt) aKt[nt] = Mma<T>::mma(af, frag_colk_lds(sQ, LDK, 16 * nt, ks), aKt[nt]);
+    }
+  }
+  // dKb = T^T dW (rows s = 16w): dk += beta e^gamma dKb, dbeta / dgamma terms
+  {
+    f32x4 aKb[NTK];
+#pragma unroll
+    for (int nt = 0; nt < NTK; ++nt) aKb[nt] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < 64; ks += KW) {
+      const frag at = frag_colk_lds(sT, L64, rw, ks);
+#pragma unroll
+      for (int nt = 0; nt < NTK; ++nt) aKb[nt] = Mma<T>::mma(at, frag_rowk(sdWT, L64, 16 * nt, ks), aKb[nt]);
+    }
+    float sr[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nt = 0; nt < NTK; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + i, dk = 16 * nt + acc_col();
+        sr[i] += to_f32(sK[r * LDK + dk]) * aKb[nt][i];
+        aKt[nt][i] += sb[r] * seg[r] * aKb[nt][i];
+      }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = r0 + i;
+      rb[i] += seg[r] * sr[i];
+      rg[i] += sb[r] * seg[r] * sr[i];
+    }
+  }
+  // dT = dT_V diag(beta) + (dW K^T) diag(beta e^gamma), rows 16w
+  f32x4 aT[4];
+  {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) aT[nt] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < DK; ks += KW) {
+      const frag af = frag_colk_lds(sdWT, L64, rw, ks);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) aT[nt] = Mma<T>::mma(af, frag_rowk(sK, LDK, 16 * nt, ks), aT[nt]);
+    }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int s = 16 * nt + acc_col();
+        aT[nt][i] = aTV[nt][i] * sb[s] + aT[nt][i] * sb[s] * seg[s];
+      }
+  }
+  __syncthreads();  // all reads of sQ, sdQKT, sdWT done
+  T* sTT = sQ;      // dT^T (s, r)
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) store_acc_t(sTT, L64, rw, 16 * nt, aT[nt]);
+  __syncthreads();
+  // Y = T^T dT (rows a = 16w) -> LDS as Y^T
+  {
+    f32x4 aY[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) aY[nt] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < 64; ks += KW) {
+      const frag at = frag_colk_lds(sT, L64, rw, ks);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) aY[nt] = Mma<T>::mma(at, frag_rowk(sTT, L64, 16 * nt, ks), aY[nt]);
+    }
+    T* sYT = sdQKT;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) store_acc_t(sYT, L64, rw, 16 * nt, aY[nt]);
+  }
+  __syncthreads();
+  // dA = -(Y T^T) strictly lower; K K^T; dbeta, dgamma terms; G -> LDS as G^T
+  {
+    const T* sYT = sdQKT;
+    f32x4 aA[4], aKK[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) aA[nt] = aKK[nt] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < 64; ks += KW) {
+      const frag ay = frag_colk_lds(sYT, L64, rw, ks);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) aA[nt] = Mma<T>::mma(ay, frag_rowk(sT, L64, 16 * nt, ks), aA[nt]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < DK; ks += KW) {
+      const frag ak = frag_rowk(sK, LDK, rw, ks);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) aKK[nt] = Mma<T>::mma(ak, frag_rowk(sK, LDK, 16 * nt, ks), aKK[nt]);
+    }
+    T* sGT = sdWT;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      f32x4 G;
+      float cs = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + i, s = 16 * nt + acc_col();
+        float gv = 0.f;
+        if (s < r) {
+          const float Gm = expf(sg[r] - sg[s]);
+          const float dA = -aA[nt][i];
+          rb[i] += dA * aKK[nt][i] * Gm;
+          const float X = dA * sb[r] * aKK[nt][i] * Gm;
+          rg[i] += X;
+          cs += X;
+          gv = dA * sb[r] * Gm;
+        }
+        G[i] = gv;
+      }
+      cs = sum4g(cs);
+      if (l < 16) sRed[1 * 256 + w * 64 + 16 * nt + l] = cs;
+      store_acc_t(sGT, L64, rw, 16 * nt, G);
+    }
+  }
+  // per-wave gamma_L partials (lanes 0..63 summed)
+  {
+    const float xh = sum4g(sum16(gLh));
+    const float xy = sum4g(sum16(gLy));
+    if (l == 0) {
+      sMisc[w] = xh;
+      sMisc[4 + w] = xy;
+    }
+  }
+  __syncthreads();
+  // dk += G K + G^T K, write dk
+  {
+    const T* sGT = sdWT;
+#pragma unroll
+    for (int ks = 0; ks < 64; ks += KW) {
+      const frag a1 = frag_colk_lds(sGT, L64, rw, ks);
+      const frag a2 = frag_rowk(sGT, L64, rw, ks);
+#pragma unroll
+      for (int nt = 0; nt < NTK; ++nt) {
+        const frag bk = frag_colk_lds(sK, LDK, 16 * nt, ks);
+        aKt[nt] = Mma<T>::mma(a1, bk, aKt[nt]);
+        aKt[nt] = Mma<T>::mma(a2, bk, aKt[nt]);
+      }
+    }
+    T* dkp = (T*)a.dk;
+#pragma unroll
+    for (int nt = 0; nt < NTK; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + i;
+        if (r < len) dkp[((int64_t)(t0 + r) * H + h) * DK + 16 * nt + acc_col()] = from_f32<T>(aKt[nt][i]);
+      }
+  }
+  // row sums -> LDS (one writer per row), then dbeta, dgamma -> dg
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    rg[i] = sum16(rg[i]);
+    rb[i] = sum16(rb[i]);
+  }
+  __syncthreads();
+  float* sRG = (float*)sQ;        // phase-2 LDS is free now
+  float* sRB = sRG + 64;
+  if ((l & 15) == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sRG[r0 + i] = rg[i];
+      sRB[r0 + i] = rb[i];
+    }
+  }
+  __syncthreads();
+  if (w == 0) {
+    float dgam = sRG[l] - (sRed[0 * 256 + 0 * 64 + l] + sRed[0 * 256 + 1 * 64 + l] + sRed[0 * 256 + 2 * 64 + l] +
+                           sRed[0 * 256 + 3 * 64 + l]) -
+                 (sRed[1 * 256 + 0 * 64 + l] + sRed[1 * 256 + 1 * 64 + l] + sRed[1 * 256 + 2 * 64 + l] +
+                  sRed[1 * 256 + 3 * 64 + l]);
+    if (l == 63) {
+      // gamma_L terms: e^{gamma_L} <dh, h> and sum_r E_r rowsum(K * Delta dh^T)
+      dgam += expf(sg[63]) * (sMisc[0] + sMisc[1] + sMisc[2] + sMisc[3]) +
+              (sMisc[4] + sMisc[5] + sMisc[6] + sMisc[7]);
+    }
+    const float dgv = wave_suffix_scan(dgam);
+    if (l < len) {
+      a.dg[(int64_t)(t0 + l) * H + h] = dgv;
+      a.dbeta[(int64_t)(t0 + l) * H + h] = sRB[l];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <typename T, int DK>
+static hipError_t launch_scan_bwd_t(const ScanBwdArgs& a, int dvt, hipStream_t st) {
+  const int grid = a.geo.N * a.geo.H * (a.DV / dvt);
+  if (grid == 0) return hipSuccess;
+  if (dvt == 16) hipLaunchKernelGGL((k_scan_bwd<T, DK, 16>), dim3(grid), dim3(256), 0, st, a);
+  else if (dvt == 32) hipLaunchKernelGGL((k_scan_bwd<T, DK, 32>), dim3(grid), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((k_scan_bwd<T, DK, 64>), dim3(grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan_bwd(const ScanBwdArgs& a, bool f32, int DK, int dvt, hipStream_t st) {
+  if (f32) return DK == 64 ? launch_scan_bwd_t<float, 64>(a, dvt, st) : launch_scan_bwd_t<float, 128>(a, dvt, st);
+  return DK == 64 ? launch_scan_bwd_t<bf16, 64>(a, dvt, st) : launch_scan_bwd_t<bf16, 128>(a, dvt, st);
+}
+
+template <typename T, int DK>
+static size_t grad_smem() {
+  constexpr int P = pad_of<T>();
+  constexpr int LDK = DK + P, L64 = 64 + P, DVB = dvb_of<T>(), LDV = DVB + P;
+  constexpr int PH1 = (DVB * LDK + DK * LDV + DVB * L64 + 2 * 64 * LDV) * (int)sizeof(T);
+  constexpr int PH2 = (2 * 64 * LDK + DK * L64 + 64 * L64) * (int)sizeof(T);
+  return 64 * L64 * sizeof(T) + (4 * 64 + 2 * 4 * 64 + 8) * 4 + cmax(PH1, PH2);
+}
+
+template <typename T, typename HS, int DK>
+static hipError_t launch_grad_t(const GradArgs& a, hipStream_t st) {
+  const size_t sm = grad_smem<T, DK>();
+  hipError_t e = hipFuncSetAttribute((const void*)k_grad<T, HS, DK>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_grad<T, HS, DK>), dim3(a.geo.nchunks, a.geo.H), dim3(256), sm, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_grad(const GradArgs& a, bool f32, int hs_dtype, int DK, hipStream_t st) {
+  if (f32) return DK == 64 ? launch_grad_t<float, float, 64>(a, st) : launch_grad_t<float, float, 128>(a, st);
+  if (hs_dtype == GDR_F32) return DK == 64 ? launch_grad_t<bf16, float, 64>(a, st) : launch_grad_t<bf16, float, 128>(a, st);
+  if (hs_dtype == GDR_F16) return DK == 64 ? launch_grad_t<bf16, f16, 64>(a, st) : launch_grad_t<bf16, f16, 128>(a, st);
+  return DK == 64 ? launch_grad_t<bf16, bf16, 64>(a, st) : launch_grad_t<bf16, bf16, 128>(a, st);
+}
+
+}  // namespace gdr

@@ -1,0 +1,254 @@
+// gdr_device.h -- device-side building blocks for the gfx950 (CDNA4) kernels
+// of the chunked gated delta rule: MFMA wrappers, operand-fragment loads from
+// LDS and global memory, accumulator-tile element maps, wavefront scans and
+// the chunk geometry of fixed-length and packed variable-length batches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdr {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16;
+typedef __bf16 bf16;
+
+#define GDR_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+// ---------------------------------------------------------------------------
+// element conversions
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+template <> __device__ __forceinline__ f16 from_f32<f16>(float x) { return (f16)x; }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(f16 x) { return (float)x; }
+
+// ---------------------------------------------------------------------------
+// MFMA: 16x16 output tiles.  Lane l supplies A[row l&15][k-slice(l>>4)] and
+// B[k-slice(l>>4)][col l&15]; the fp32 result holds C[4*(l>>4)+i][l&15].
+// bf16 operands use v_mfma_f32_16x16x32_bf16 (8 k per lane), fp32 operands
+// v_mfma_f32_16x16x4_f32 (1 k per lane).
+
+template <typename T> struct Mma;
+template <> struct Mma<bf16> {
+  static constexpr int KW = 32;   // k per instruction
+  static constexpr int KPL = 8;   // k per lane
+  typedef bf16x8 frag;
+  static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ frag neg(frag a) {
+    typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+    u16x8 u = __builtin_bit_cast(u16x8, a);
+    u ^= (unsigned short)0x8000;
+    return __builtin_bit_cast(frag, u);
+  }
+  static __device__ __forceinline__ frag zero() {
+    typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+    return __builtin_bit_cast(frag, (u16x8)(unsigned short)0);
+  }
+};
+template <> struct Mma<float> {
+  static constexpr int KW = 4;
+  static constexpr int KPL = 1;
+  typedef float frag;
+  static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ frag neg(frag a) { return -a; }
+  static __device__ __forceinline__ frag zero() { return 0.0f; }
+};
+
+__device__ __forceinline__ f32x4 zero4() { return (f32x4){0.f, 0.f, 0.f, 0.f}; }
+
+// ---------------------------------------------------------------------------
+// Operand fragments.
+//
+// "RowK" view: element (i, k) lives at p[i * ld + k] (k contiguous).
+// "ColK" view: element (i, k) lives at p[k * ld + i] (i contiguous).
+// A fragment for rows i0..i0+15 and k-block k0..k0+KW-1 gives lane l the
+// elements (i0 + (l & 15), k0 + KPL*(l >> 4) + j), j < KPL.
+
+// RowK from LDS or global: bf16 -> one 16-byte load.
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag frag_rowk(const T* p, int ld, int i0, int k0) {
+  const int l = lane_id();
+  const T* q = p + (int64_t)(i0 + (l & 15)) * ld + k0 + Mma<T>::KPL * (l >> 4);
+  if constexpr (Mma<T>::KPL == 8) {
+    return *reinterpret_cast<const bf16x8*>(q);
+  } else {
+    return *q;
+  }
+}
+
+// RowK from global memory with rows >= nrows reading as zero.
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag frag_rowk_masked(const T* p, int64_t ld, int i0,
+                                                                 int k0, int nrows) {
+  const int l = lane_id();
+  const int i = i0 + (l & 15);
+  if (i >= nrows) return Mma<T>::zero();
+  const T* q = p + (int64_t)i * ld + k0 + Mma<T>::KPL * (l >> 4);
+  if constexpr (Mma<T>::KPL == 8) {
+    return *reinterpret_cast<const bf16x8*>(q);
+  } else {
+    return *q;
+  }
+}
+
+// ColK from LDS.  bf16 uses the gfx950 transposing LDS read
+// ds_read_b64_tr_b16: within each 16-lane group, lane j addresses the 4
+// contiguous elements at (row j>>2, cols 4*(j&3)..+3) of a 4 x 16 block and
+// lane i receives column i of that block (4 consecutive rows).  Two such
+// reads give the 8 k values of a bf16 fragment.  Requires ld % 4 == 0 and
+// i0 % 4 == 0 (8-byte aligned addresses).
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag frag_colk_lds(const T* p, int ld, int i0, int k0) {
+  const int l = lane_id();
+  if constexpr (Mma<T>::KPL == 8) {
+    const int j = l & 15;
+    const int kb = k0 + 8 * (l >> 4) + (j >> 2);
+    const int ib = i0 + 4 * (j & 3);
+    const GDR_LDS i16x4* a0 = (const GDR_LDS i16x4*)((const GDR_LDS T*)p + kb * ld + ib);
+    const GDR_LDS i16x4* a1 = (const GDR_LDS i16x4*)((const GDR_LDS T*)p + (kb + 4) * ld + ib);
+    i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GDR_LDS i16x4*)a0);
+    i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GDR_LDS i16x4*)a1);
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    i16x8 r = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, r);
+  } else {
+    return p[(k0 + (l >> 4)) * ld + i0 + (l & 15)];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Accumulator tile element map: lane l holds C[r0 + i][c], i < 4, with
+// r0 = 4*(l>>4), c = l & 15 (relative to the tile origin).
+__device__ __forceinline__ int acc_row0() { return 4 * (lane_id() >> 4); }
+__device__ __forceinline__ int acc_col() { return lane_id() & 15; }
+
+// Store an accumulator tile transposed: dst[(c0 + c) * ld + (r0 + r0l + i)],
+// i.e. the 4 consecutive rows of the lane become 4 contiguous elements.
+template <typename T>
+__device__ __forceinline__ void store_acc_t(T* dst, int ld, int r0, int c0, f32x4 v) {
+  T* q = dst + (int64_t)(c0 + acc_col()) * ld + r0 + acc_row0();
+  if constexpr (sizeof(T) == 2) {
+    typedef T t4 __attribute__((ext_vector_type(4)));
+    t4 w = {(T)v[0], (T)v[1], (T)v[2], (T)v[3]};
+    *reinterpret_cast<t4*>(q) = w;
+  } else {
+    *reinterpret_cast<f32x4*>(q) = v;
+  }
+}
+
+// Store an accumulator tile in its own orientation: dst[(r0 + i) * ld + c0 + c].
+template <typename T>
+__device__ __forceinline__ void store_acc(T* dst, int64_t ld, int r0, int c0, f32x4 v) {
+  T* q = dst + (int64_t)(r0 + acc_row0()) * ld + c0 + acc_col();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q[i * ld] = from_f32<T>(v[i]);
+}
+
+// ---------------------------------------------------------------------------
+// Wavefront scans over 64 lanes.
+__device__ __forceinline__ float wave_incl_scan(float x) {
+  const int l = lane_id();
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    float y = __shfl_up(x, d, 64);
+    if (l >= d) x += y;
+  }
+  return x;
+}
+// suffix sum: out_l = sum_{m >= l} x_m
+__device__ __forceinline__ float wave_suffix_scan(float x) {
+  const int l = lane_id();
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    float y = __shfl_down(x, d, 64);
+    if (l + d < 64) x += y;
+  }
+  return x;
+}
+// sum over the 16 lanes sharing l >> 4
+__device__ __forceinline__ float sum16(float x) {
+  x += __shfl_xor(x, 1, 64);
+  x += __shfl_xor(x, 2, 64);
+  x += __shfl_xor(x, 4, 64);
+  x += __shfl_xor(x, 8, 64);
+  return x;
+}
+// sum over the 4 lane groups sharing l & 15
+__device__ __forceinline__ float sum4g(float x) {
+  x += __shfl_xor(x, 16, 64);
+  x += __shfl_xor(x, 32, 64);
+  return x;
+}
+
+// ---------------------------------------------------------------------------
+// Chunk geometry.  Chunks hold C = 64 tokens and never straddle sequences;
+// the last chunk of a sequence may be partial.  Fixed-length batches use
+// arithmetic; packed batches use the device chunk table built by the plan
+// kernel (seq_chunk[n] = first chunk slot of sequence n, chunk_seq[c] =
+// sequence of slot c or -1).
+constexpr int CH = 64;
+
+struct Geo {
+  int H;
+  int N;            // sequences
+  int T_fixed;      // tokens per sequence (fixed-length batches)
+  int nc_per_seq;   // chunks per sequence (fixed-length batches)
+  int nchunks;      // chunk slots (grid size of chunk-parallel kernels)
+  int T_total;      // packed batches: size of the token dimension (clamps cu_seqlens)
+  const int* cu;        // packed: cu_seqlens [N+1], else nullptr
+  const int* seq_chunk; // packed: [N+1]
+  const int* chunk_seq; // packed: [nchunks]
+};
+
+__device__ __forceinline__ bool chunk_lookup(const Geo& g, int ci, int& n, int& t0, int& len) {
+  if (g.cu == nullptr) {
+    if (g.nc_per_seq <= 0) return false;
+    n = ci / g.nc_per_seq;
+    const int j = ci - n * g.nc_per_seq;
+    t0 = n * g.T_fixed + j * CH;
+    len = min(CH, g.T_fixed - j * CH);
+    return len > 0;
+  }
+  n = g.chunk_seq[ci];
+  if (n < 0) return false;
+  const int j = ci - g.seq_chunk[n];
+  // cu_seqlens is clamped into [0, T_total] so that a contract violation can
+  // never address tokens outside the buffers
+  const int s = min(max(g.cu[n], 0), g.T_total);
+  const int e = min(max(g.cu[n + 1], s), g.T_total);
+  t0 = s + j * CH;
+  len = min(CH, e - t0);
+  return len > 0;
+}
+
+// chunk slots [c0, c0 + nc) and tokens [ts, ts + tl) of sequence n
+__device__ __forceinline__ void seq_range(const Geo& g, int n, int& c0, int& nc, int& ts, int& tl) {
+  if (g.cu == nullptr) {
+    c0 = n * g.nc_per_seq;
+    nc = g.nc_per_seq;
+    ts = n * g.T_fixed;
+    tl = g.T_fixed;
+  } else {
+    c0 = g.seq_chunk[n];
+    nc = g.seq_chunk[n + 1] - c0;
+    ts = min(max(g.cu[n], 0), g.T_total);
+    tl = min(max(g.cu[n + 1], ts), g.T_total) - ts;
+    nc = min(nc, (tl + CH - 1) / CH);
+  }
+}
+
+}  // namespace gdr

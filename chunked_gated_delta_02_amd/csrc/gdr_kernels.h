@@ -1,0 +1,177 @@
+// gdr_kernels.h -- kernel argument blocks, LDS staging helpers and launcher
+// declarations shared by the forward and backward kernel files.
+#pragma once
+
+#include "gdr_device.h"
+#include "libgdr.h"
+
+#define GDR_MAX_SEQS 8192
+
+namespace gdr {
+
+// LDS row padding in elements: 16 bytes for 16-bit tiles (keeps 16-byte
+// aligned rows for ds_read_b128 and shifts consecutive rows by 4 banks),
+// 16 bytes for fp32 tiles as well.
+template <typename T> constexpr int pad_of() { return sizeof(T) == 2 ? 8 : 4; }
+// value-dim block processed at once by the chunk-parallel kernels
+template <typename T> constexpr int dvb_of() { return sizeof(T) == 2 ? 64 : 32; }
+constexpr int cmax(int x, int y) { return x > y ? x : y; }
+
+struct WyArgs {
+  Geo geo;
+  int DV;
+  float scale;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* beta;
+  const float* g;
+  float* gam;   // [slot][H][64]
+  void* W;      // [slot][H][64][DK]
+  void* KtT;    // [slot][H][DK][64]
+  void* UT;     // [slot][H][DV][64]
+  float* Tm;    // [slot][H][64][64]       (backward)
+  void* WT;     // [slot][H][DK][64]       (backward)
+  void* PsT;    // [slot][H][64][64]       (backward)
+  void* QgsT;   // [slot][H][DK][64]       (backward)
+};
+
+struct ScanFwdArgs {
+  Geo geo;
+  int DV;
+  int layout;        // 0: KV, 1: VK for h0 / hT
+  const float* h0;   // nullable
+  float* hT;         // nullable
+  const float* gam;
+  const void* W;
+  const void* KtT;
+  const void* UT;
+  void* hs;          // [slot][H][DV][DK] snapshots (state at chunk start), nullable
+  void* Dt;          // [slot][H][DV][64] Delta^T, nullable
+};
+
+struct OutArgs {
+  Geo geo;
+  int DV;
+  float scale;
+  const void* q;
+  const void* k;
+  const float* gam;
+  const void* hs;
+  const void* Dt;
+  void* o;
+};
+
+struct ScanBwdArgs {
+  Geo geo;
+  int DV;
+  int layout;
+  const float* dhT;  // nullable
+  float* dh0;        // nullable
+  const void* k;
+  const void* dO;
+  const float* gam;
+  const void* PsT;
+  const void* QgsT;
+  const void* WT;
+  void* dhs;         // [slot][H][DK][DV] gradient of the state at chunk end
+  void* dD;          // [slot][H][64][DV] gradient of Delta
+};
+
+struct GradArgs {
+  Geo geo;
+  int DV;
+  float scale;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dO;
+  const float* beta;
+  const float* gam;
+  const void* W;
+  const void* UT;
+  const float* Tm;
+  const void* hs;
+  const void* dhs;
+  const void* dD;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dbeta;
+  float* dg;
+};
+
+// ---------------------------------------------------------------------------
+// LDS staging.  NR rows of NC elements from global (row stride gstride
+// elements) into LDS (row stride ld); rows >= nvalid are zero.  16-byte
+// accesses, all 256 threads.
+template <typename T, int NC, int NR = 64>
+__device__ __forceinline__ void load_rows(T* s, int ld, const T* g, int64_t gstride, int nvalid) {
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int PER_ROW = NC / VEC;
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  for (int e = threadIdx.x; e < NR * PER_ROW; e += blockDim.x) {
+    const int r = e / PER_ROW, c = (e - r * PER_ROW) * VEC;
+    f4 v = {0.f, 0.f, 0.f, 0.f};
+    if (r < nvalid) v = *reinterpret_cast<const f4*>(g + r * gstride + c);
+    *reinterpret_cast<f4*>(s + r * ld + c) = v;
+  }
+}
+
+// Same with element conversion from S (global) to T (LDS).
+template <typename S, typename T, int NC, int NR>
+__device__ __forceinline__ void load_rows_conv(T* s, int ld, const S* g, int64_t gstride, int nvalid) {
+  if constexpr (__is_same(S, T)) {
+    load_rows<T, NC, NR>(s, ld, (const T*)g, gstride, nvalid);
+  } else {
+    constexpr int VEC = 4;
+    constexpr int PER_ROW = NC / VEC;
+    for (int e = threadIdx.x; e < NR * PER_ROW; e += blockDim.x) {
+      const int r = e / PER_ROW, c = (e - r * PER_ROW) * VEC;
+      float v[4] = {0.f, 0.f, 0.f, 0.f};
+      if (r < nvalid) {
+        const S* q = g + r * gstride + c;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = to_f32(q[j]);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s[r * ld + c + j] = from_f32<T>(v[j]);
+    }
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store8(T* dst, const float* v) {
+  if constexpr (sizeof(T) == 2) {
+    typedef T t8 __attribute__((ext_vector_type(8)));
+    t8 w;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w[j] = from_f32<T>(v[j]);
+    *reinterpret_cast<t8*>(dst) = w;
+  } else {
+    *reinterpret_cast<f32x4*>(dst) = (f32x4){v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4*>(dst + 4) = (f32x4){v[4], v[5], v[6], v[7]};
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ f32x4 load4f(const T* p) {
+  if constexpr (sizeof(T) == 2) {
+    typedef T t4 __attribute__((ext_vector_type(4)));
+    const t4 v = *reinterpret_cast<const t4*>(p);
+    return (f32x4){to_f32(v[0]), to_f32(v[1]), to_f32(v[2]), to_f32(v[3])};
+  } else {
+    return *reinterpret_cast<const f32x4*>(p);
+  }
+}
+
+// launchers (return the HIP error of the launch)
+hipError_t launch_plan(const int* cu, int N, int T_total, int nchunks, int* seq_chunk, int* chunk_seq,
+                       hipStream_t st);
+hipError_t launch_wy(const WyArgs& a, bool f32, int DK, bool bwd, hipStream_t st);
+hipError_t launch_scan_fwd(const ScanFwdArgs& a, bool f32, int hs_dtype, int DK, int dvt, hipStream_t st);
+hipError_t launch_out(const OutArgs& a, bool f32, int hs_dtype, int DK, hipStream_t st);
+hipError_t launch_scan_bwd(const ScanBwdArgs& a, bool f32, int DK, int dvt, hipStream_t st);
+hipError_t launch_grad(const GradArgs& a, bool f32, int hs_dtype, int DK, hipStream_t st);
+
+}  // namespace gdr

@@ -1,0 +1,164 @@
+"""The C-ABI boundary on the host: exports, argument validation, workspace
+sizing.  No call here reaches a GPU -- every error path returns before any
+launch, which is what these tests check."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from chunked_gated_delta_02_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libgdr.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from chunked_gated_delta_02_amd import build
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdr_[a-z_0-9]+)\s*\(", text)))
+
+
+def good(**kw):
+    p = _lib.gdr_problem()
+    p.batch, p.seqlen, p.num_seqs, p.varlen, p.heads = 2, 4096, 2, 0, 16
+    p.dk, p.dv, p.chunk = 128, 128, 64
+    p.io_dtype, p.h_store_dtype, p.layout, p.cp_segments, p.scale = _lib.GDR_BF16, _lib.GDR_F32, 0, 1, 0.0
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def test_every_declared_function_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_valid_problems(lib):
+    assert _lib.gdr_check(good()) == _lib.GDR_OK
+    assert _lib.gdr_check(good(io_dtype=_lib.GDR_F32, dk=64, dv=64)) == _lib.GDR_OK
+    assert _lib.gdr_check(good(varlen=1, batch=1, num_seqs=8, seqlen=30000)) == _lib.GDR_OK
+    assert _lib.gdr_check(good(dv=256, h_store_dtype=_lib.GDR_F16)) == _lib.GDR_OK
+    assert _lib.gdr_check(good(seqlen=0)) == _lib.GDR_OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0, num_seqs=0), _lib.GDR_ERR_INVALID_ARG),
+    (dict(seqlen=-1), _lib.GDR_ERR_INVALID_ARG),
+    (dict(heads=0), _lib.GDR_ERR_INVALID_ARG),
+    (dict(num_seqs=3), _lib.GDR_ERR_INVALID_ARG),
+    (dict(varlen=1), _lib.GDR_ERR_INVALID_ARG),          # batch 2 with varlen
+    (dict(varlen=1, batch=1, num_seqs=0), _lib.GDR_ERR_INVALID_ARG),
+    (dict(varlen=1, batch=1, num_seqs=100000), _lib.GDR_ERR_UNSUPPORTED),
+    (dict(varlen=2), _lib.GDR_ERR_INVALID_ARG),
+    (dict(chunk=32), _lib.GDR_ERR_UNSUPPORTED),
+    (dict(dk=96), _lib.GDR_ERR_UNSUPPORTED),
+    (dict(dv=100), _lib.GDR_ERR_UNSUPPORTED),
+    (dict(dv=1024), _lib.GDR_ERR_UNSUPPORTED),
+    (dict(io_dtype=_lib.GDR_F16), _lib.GDR_ERR_UNSUPPORTED),
+    (dict(io_dtype=7), _lib.GDR_ERR_UNSUPPORTED),
+    (dict(h_store_dtype=9), _lib.GDR_ERR_INVALID_ARG),
+    (dict(io_dtype=_lib.GDR_F32, h_store_dtype=_lib.GDR_F16), _lib.GDR_ERR_UNSUPPORTED),
+    (dict(layout=2), _lib.GDR_ERR_INVALID_ARG),
+    (dict(cp_segments=0), _lib.GDR_ERR_INVALID_ARG),
+])
+def test_invalid_problems(lib, kw, status):
+    assert _lib.gdr_check(good(**kw)) == status
+    assert _lib.gdr_fwd_workspace_bytes(good(**kw)) == 0
+    assert _lib.last_error() != ""
+
+
+def test_null_problem(lib):
+    assert lib.gdr_check(None) == _lib.GDR_ERR_INVALID_ARG
+
+
+FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced: calls fail before any launch
+
+
+def fwd_args(p, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=FAKE, cu=0, h0=0, o=FAKE, hT=0, hs=0,
+             ws=FAKE, ws_bytes=_lib.gdr_fwd_workspace_bytes(p), stream=0)
+    a.update(kw)
+    return a
+
+
+def call_fwd(p, a):
+    return _lib.gdr_chunk_fwd(p, a["q"], a["k"], a["v"], a["beta"], a["g"], a["cu"], a["h0"], a["o"],
+                              a["hT"], a["hs"], a["ws"], a["ws_bytes"], a["stream"], check=False)
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "beta", "g", "o"])
+def test_fwd_null_required_pointer(lib, field):
+    p = good()
+    assert call_fwd(p, fwd_args(p, **{field: 0})) == _lib.GDR_ERR_INVALID_ARG
+
+
+def test_fwd_misaligned_pointer(lib):
+    p = good()
+    assert call_fwd(p, fwd_args(p, v=FAKE + 2)) == _lib.GDR_ERR_INVALID_ARG
+    assert call_fwd(p, fwd_args(p, h0=FAKE + 8)) == _lib.GDR_ERR_INVALID_ARG
+
+
+def test_fwd_workspace_too_small_or_missing(lib):
+    p = good()
+    need = _lib.gdr_fwd_workspace_bytes(p)
+    assert call_fwd(p, fwd_args(p, ws_bytes=need - 1)) == _lib.GDR_ERR_WORKSPACE
+    assert call_fwd(p, fwd_args(p, ws=0)) == _lib.GDR_ERR_WORKSPACE
+
+
+def test_fwd_cu_seqlens_consistency(lib):
+    p = good()
+    assert call_fwd(p, fwd_args(p, cu=FAKE)) == _lib.GDR_ERR_INVALID_ARG
+    pv = good(varlen=1, batch=1, num_seqs=4)
+    assert call_fwd(pv, fwd_args(pv)) == _lib.GDR_ERR_INVALID_ARG
+
+
+def test_fwd_unsupported_context_parallel_reports(lib):
+    p = good(cp_segments=4)
+    st = _lib.gdr_check(p)
+    assert st in (_lib.GDR_OK, _lib.GDR_ERR_UNSUPPORTED)
+
+
+def test_bwd_validation(lib):
+    p = good()
+    ws = _lib.gdr_bwd_workspace_bytes(p, False)
+    args = [FAKE] * 5 + [0, 0, 0, FAKE, 0] + [FAKE] * 5 + [0]
+    st = _lib.gdr_chunk_bwd(p, *args, FAKE, ws - 1, 0, check=False)
+    assert st == _lib.GDR_ERR_WORKSPACE
+    bad = list(args)
+    bad[8] = 0  # dO
+    assert _lib.gdr_chunk_bwd(p, *bad, FAKE, ws, 0, check=False) == _lib.GDR_ERR_INVALID_ARG
+
+
+def test_workspace_sizes(lib):
+    p = good()
+    f = _lib.gdr_fwd_workspace_bytes(p)
+    b0 = _lib.gdr_bwd_workspace_bytes(p, False)
+    b1 = _lib.gdr_bwd_workspace_bytes(p, True)
+    hs = _lib.gdr_h_saved_bytes(p)
+    nchunks = 2 * 64
+    assert hs == nchunks * 16 * 128 * 128 * 4
+    assert b0 - b1 >= hs
+    assert f > 0 and b1 > 0
+    assert _lib.gdr_h_saved_bytes(good(h_store_dtype=_lib.GDR_F16)) == hs // 2
+    # packed batches: chunk slots bounded by ceil(T/64) + N without reading cu_seqlens
+    pv = good(varlen=1, batch=1, num_seqs=8, seqlen=1000)
+    assert _lib.gdr_h_saved_bytes(pv) == (16 + 8) * 16 * 128 * 128 * 4
+    assert _lib.gdr_fwd_workspace_bytes(good(seqlen=8192)) > f
+
+
+def test_status_strings_and_version(lib):
+    assert _lib.status_string(_lib.GDR_OK) == "GDR_OK"
+    assert _lib.status_string(_lib.GDR_ERR_WORKSPACE) == "GDR_ERR_WORKSPACE"
+    assert _lib.gdr_version() >= 100

@@ -1,0 +1,186 @@
+"""GPU parity of libgdr against the fp64 oracle (element-wise, normwise
+relative error per output tensor: <= 1e-5 on the fp32 path, <= 5e-3 on the
+bf16-input / fp32-state path)."""
+import numpy as np
+import pytest
+import torch
+
+from chunked_gated_delta_02_amd import inputs as gin
+from chunked_gated_delta_02_amd import ops
+from tests.gdr_cases import compare, rel, run_gpu, run_oracle, say, to64
+
+pytestmark = pytest.mark.gpu
+
+C = gin.CONFIGS
+
+# Reduced-size versions of the five workloads: several chunks, ragged tails,
+# every layout / state option, small enough for the oracle in seconds.
+SMALL = {
+    "cfg0_tiny_fp32": C[0],
+    "cfg1_fixed_bf16_ragged": C[1].replace(name="cfg1_small", B=2, T=333, H=3),
+    "cfg2_varlen_bf16": C[2].replace(name="cfg2_small", H=4, lengths=[70, 0, 1, 200, 129, 64],
+                                     len_range=None),
+    "cfg3_slowdecay_f32state": C[3].replace(name="cfg3_small", T=1000, H=2, cp_segments=1),
+    "cfg3_slowdecay_f16state": C[3].replace(name="cfg3_small_f16", T=1000, H=2, cp_segments=1,
+                                            h_store="f16"),
+    "cfg4_widev_bf16": C[4].replace(name="cfg4_small", B=2, T=200, H=2),
+    "fp32_dk128": C[0].replace(name="fp32_dk128", B=2, T=150, H=2, DK=128, DV=128, layout="KV"),
+    "fp32_dv192_varlen": C[0].replace(name="fp32_dv192_varlen", H=2, DK=64, DV=192,
+                                      lengths=[65, 3, 128], layout="KV"),
+    "bf16_dk64_dv192": C[1].replace(name="bf16_dk64_dv192", B=1, T=190, H=2, DK=64, DV=192,
+                                    has_h0=True),
+    "bf16_bf16state": C[1].replace(name="bf16_bf16state", B=1, T=260, H=2, h_store="bf16"),
+    "bf16_short_T10": C[1].replace(name="bf16_T10", B=3, T=10, H=2, has_h0=True),
+    "bf16_exact_T64": C[1].replace(name="bf16_T64", B=1, T=64, H=2, layout="VK", has_h0=True),
+    "bf16_no_dhT": C[1].replace(name="bf16_no_dhT", B=1, T=130, H=2, has_dhT=False),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib_built():
+    from chunked_gated_delta_02_amd import _lib
+    _lib.load()
+
+
+@pytest.mark.parametrize("case", sorted(SMALL))
+def test_parity_small(case):
+    w = SMALL[case]
+    say("[case] %s" % case)
+    inp = gin.generate(w)
+    got = run_gpu(w, inp)
+    ref = run_oracle(w, inp)
+    compare(w, got, ref)
+
+
+def test_backward_with_saved_states_equals_recompute():
+    w = SMALL["cfg1_fixed_bf16_ragged"]
+    say("[case] saved-vs-recompute %s" % w.name)
+    inp = gin.generate(w)
+    a = run_gpu(w, inp, saved=True)
+    b = run_gpu(w, inp, saved=False)
+    for name in a:
+        np.testing.assert_array_equal(a[name], b[name], err_msg=name)
+
+
+def test_bitwise_reproducible():
+    w = SMALL["cfg2_varlen_bf16"]
+    say("[case] determinism %s" % w.name)
+    inp = gin.generate(w)
+    a = run_gpu(w, inp)
+    for _ in range(3):
+        b = run_gpu(w, inp)
+        for name in a:
+            np.testing.assert_array_equal(a[name], b[name], err_msg=name)
+
+
+def test_layouts_agree():
+    w = SMALL["cfg4_widev_bf16"]
+    say("[case] KV vs VK %s" % w.name)
+    inp = gin.generate(w)
+    a = run_gpu(w, inp)
+    inp2 = dict(inp)
+    inp2["h0"] = inp["h0"].transpose(-1, -2).contiguous()
+    inp2["dhT"] = inp["dhT"].transpose(-1, -2).contiguous()
+    b = run_gpu(w.replace(layout="VK"), inp2)
+    for name in ("o", "dq", "dk", "dv", "dbeta", "dg"):
+        np.testing.assert_array_equal(a[name], b[name], err_msg=name)
+    np.testing.assert_array_equal(a["hT"], np.swapaxes(b["hT"], -1, -2))
+    np.testing.assert_array_equal(a["dh0"], np.swapaxes(b["dh0"], -1, -2))
+
+
+def test_varlen_equals_separate_sequences():
+    w = SMALL["cfg2_varlen_bf16"]
+    say("[case] varlen vs per-sequence %s" % w.name)
+    inp = gin.generate(w)
+    a = run_gpu(w, inp)
+    cu = inp["cu_seqlens"].tolist()
+    for n in range(len(cu) - 1):
+        s, e = cu[n], cu[n + 1]
+        if e == s:
+            continue
+        one = dict(q=inp["q"][:, s:e], k=inp["k"][:, s:e], v=inp["v"][:, s:e],
+                   beta=inp["beta"][:, s:e], g=inp["g"][:, s:e], do=inp["do"][:, s:e],
+                   h0=inp["h0"][n:n + 1], dhT=inp["dhT"][n:n + 1], cu_seqlens=None)
+        one = {k: (v.contiguous() if isinstance(v, torch.Tensor) else v) for k, v in one.items()}
+        b = run_gpu(w.replace(lengths=None, len_range=None, B=1, T=e - s), one)
+        for name in ("o", "dq", "dk", "dv", "dbeta", "dg"):
+            assert rel(b[name], a[name][:, s:e]) < 1e-6, (n, name)
+        assert rel(b["hT"], a["hT"][n:n + 1]) < 1e-6
+        assert rel(b["dh0"], a["dh0"][n:n + 1]) < 1e-6
+
+
+def test_zero_length_sequences_hand_state_through():
+    w = C[2].replace(name="zero_len", H=2, lengths=[0, 150, 0, 7], len_range=None)
+    say("[case] zero-length sequences")
+    inp = gin.generate(w)
+    got = run_gpu(w, inp)
+    h0, dhT = to64(inp["h0"]), to64(inp["dhT"])
+    np.testing.assert_array_equal(got["hT"][0], h0[0])
+    np.testing.assert_array_equal(got["hT"][2], h0[2])
+    np.testing.assert_array_equal(got["dh0"][0], dhT[0])
+    np.testing.assert_array_equal(got["dh0"][2], dhT[2])
+    ref = run_oracle(w, inp)
+    compare(w, got, ref)
+
+
+def test_beta0_g0_reads_initial_state():
+    w = C[1].replace(name="beta0_g0", B=1, T=100, H=2, has_h0=True)
+    say("[case] beta = 0, g = 0")
+    inp = gin.generate(w)
+    inp["beta"] = torch.zeros_like(inp["beta"])
+    inp["g"] = torch.zeros_like(inp["g"])
+    got = run_gpu(w, inp)
+    h0 = to64(inp["h0"])  # KV: [N, H, DK, DV]
+    q = to64(inp["q"])
+    ref = (128 ** -0.5) * np.einsum("hkv,bthk->bthv", h0[0], q)
+    assert rel(got["o"], ref) < 5e-3
+    np.testing.assert_allclose(got["hT"], h0, rtol=0, atol=1e-6)
+
+
+def test_full_decay_and_large_gamma_range():
+    # g very negative: exp(g) underflows, the state resets inside chunks
+    w = C[1].replace(name="strong_decay", B=1, T=300, H=2, has_h0=True)
+    say("[case] strong decay")
+    inp = gin.generate(w)
+    inp["g"] = inp["g"] * 20.0 - 1.0
+    got = run_gpu(w, inp)
+    ref = run_oracle(w, inp)
+    compare(w, got, ref)
+
+
+def test_autograd_matches_explicit_backward():
+    w = SMALL["cfg1_fixed_bf16_ragged"].replace(has_h0=True)
+    say("[case] autograd")
+    inp = gin.generate(w)
+    dev = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    leaves = {n: dev[n].clone().requires_grad_(True) for n in ("q", "k", "v", "beta", "g", "h0")}
+    o, hT = ops.chunk_gdr(leaves["q"], leaves["k"], leaves["v"], leaves["beta"], leaves["g"],
+                          h0=leaves["h0"], layout=w.layout)
+    torch.autograd.backward([o, hT], [dev["do"], dev["dhT"]])
+    torch.cuda.synchronize()
+    r = ops.chunk_gdr_bwd(dev["q"], dev["k"], dev["v"], dev["beta"], dev["g"], dev["do"], h0=dev["h0"],
+                          dhT=dev["dhT"], layout=w.layout)
+    torch.cuda.synchronize()
+    for n, gname in (("q", "dq"), ("k", "dk"), ("v", "dv"), ("beta", "dbeta"), ("g", "dg"), ("h0", "dh0")):
+        assert torch.equal(leaves[n].grad, r[gname]), n
+
+
+# ---------------------------------------------------------------------------
+# full sizes of the workloads, the launch configuration the benchmark times,
+# checked on sampled heads (each head is an independent problem)
+
+FULL = {
+    "cfg1": (C[1], [0, 11]),
+    "cfg2": (C[2], [5]),
+    "cfg4": (C[4].replace(B=1), [3]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FULL))
+def test_parity_full_size_sampled_heads(name):
+    w, heads = FULL[name]
+    say("[case] full-size %s heads %s" % (w.name, heads))
+    inp = gin.generate(w)
+    got = run_gpu(w, inp)
+    ref = run_oracle(w, inp, heads=heads)
+    compare(w, got, ref, heads=heads)
