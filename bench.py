@@ -62,22 +62,25 @@ def flops_bwd(K, V, C=CH):
 
 def kernel_model(name, mode, NC, NP, NT, K, V, e, hs, C=CH):
     if name == "wy":
-        rd = NT * (K * e + V * e + 8)
-        wr = NC * (C * 4 + C * K * e + K * C * e + V * C * e)
-        fl = NC * (2 * C * C * K + C ** 3 / 3.0 + 2 * C * C * K + 2 * C * C * V)
+        # reads q, k, v, beta, g; writes gamma, W, Kt^T, U^T and P (fwd) or
+        # T, W^T, scale P^T, scale Qg^T (bwd)
+        rd = NT * (2 * K * e + V * e + 8)
+        wr = NC * (C * 4 + C * K * e + K * C * e + V * C * e + C * C * e)
+        fl = NC * (2 * C * C * K + C ** 3 / 3.0 + 2 * C * C * K + 2 * C * C * V + 2 * C * C * K)
         if mode == "bwd":
-            rd += NT * K * e
-            wr += NC * (C * C * 4 + K * C * e + C * C * e + K * C * e)
-            fl += NC * 2 * C * C * K
+            wr += NC * (C * C * 4 + K * C * e + K * C * e)
         return rd + wr, fl
     if name == "scan_fwd":
-        rd = NC * (2 * C * K * e + V * C * e + 4) + NP * K * V * 4
-        wr = NC * (K * V * hs + (V * C * e if mode == "fwd" else 0)) + NP * K * V * 4
-        return rd + wr, NC * 4 * C * K * V
-    if name == "out":
-        rd = NT * 2 * K * e + NC * (K * V * hs + V * C * e + C * 4)
-        wr = NT * V * e
-        return rd + wr, NC * (2 * C * C * K + 2 * C * K * V + 2 * C * C * V)
+        # reads W, Kt^T, U^T, gamma (+ q, P with the fused output); writes the
+        # snapshots (+ o); h0 / hT per (sequence, head)
+        rd = NC * (2 * C * K * e + V * C * e + C * 4) + NP * K * V * 4
+        wr = NC * K * V * hs + NP * K * V * 4
+        fl = NC * 4 * C * K * V
+        if mode == "fwd":
+            rd += NT * K * e + NC * C * C * e
+            wr += NT * V * e
+            fl += NC * (2 * C * K * V + 2 * C * C * V)
+        return rd + wr, fl
     if name == "scan_bwd":
         rd = NT * (K * e + V * e) + NC * (C * C * e + 2 * K * C * e + 4) + NP * K * V * 4
         wr = NC * (K * V * e + C * V * e) + NP * K * V * 4

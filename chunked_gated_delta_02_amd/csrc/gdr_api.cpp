@@ -68,12 +68,13 @@ struct Plan {
   int N = 0, NCb = 0, ncps = 0;
   bool f32 = false;
   size_t esz = 2, hsz = 4;
-  size_t seq_chunk = 0, chunk_seq = 0, gam = 0, W = 0, KtT = 0, UT = 0, hs = 0, Dt = 0;
-  size_t Tm = 0, WT = 0, PsT = 0, QgsT = 0, dhs = 0, dD = 0;
+  size_t seq_chunk = 0, chunk_seq = 0, gam = 0, Wf = 0, KtTf = 0, Ua = 0, hs = 0, Qgf = 0, Pf = 0;
+  size_t Tm = 0, WTf = 0, PsTf = 0, QgsTf = 0, Ktf = 0, dOf = 0, dhs = 0, dD = 0;
   size_t total = 0;
 };
 
-// mode 0: forward, 1: backward
+// mode 0: forward, 1: backward.  need_hs: the snapshots live in the
+// workspace (forward without h_saved, backward recomputing them).
 Plan make_plan(const gdr_problem* p, int mode, bool need_hs) {
   Plan pl;
   pl.N = p->varlen ? p->num_seqs : p->batch;
@@ -88,27 +89,33 @@ Plan make_plan(const gdr_problem* p, int mode, bool need_hs) {
     pl.NCb = p->batch * pl.ncps;
   }
   const size_t ch = (size_t)pl.NCb * p->heads;
-  const size_t DK = p->dk, DV = p->dv;
+  const size_t DK = p->dk, DV = p->dv, e = pl.esz;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
   if (p->varlen) {
     pl.seq_chunk = take(sizeof(int) * (pl.N + 1));
     pl.chunk_seq = take(sizeof(int) * (size_t)pl.NCb);
   }
-  pl.gam = take(ch * 64 * 4);
-  pl.W = take(ch * 64 * DK * pl.esz);
-  pl.KtT = take(ch * DK * 64 * pl.esz);
-  pl.UT = take(ch * DV * 64 * pl.esz);
-  if (need_hs) pl.hs = take(ch * DV * DK * pl.hsz);
+  pl.gam = take(ch * GSTRIDE * 4);
+  pl.Wf = take(ch * 64 * DK * e);
+  pl.Ua = take(ch * 64 * DV * e);
+  if (need_hs) {
+    pl.hs = take(ch * DV * DK * pl.hsz);
+    pl.KtTf = take(ch * DK * 64 * e);
+  }
   if (mode == 0) {
-    pl.Dt = take(ch * DV * 64 * pl.esz);
+    if (!need_hs) pl.KtTf = take(ch * DK * 64 * e);
+    pl.Qgf = take(ch * 64 * DK * e);
+    pl.Pf = take(ch * 64 * 64 * e);
   } else {
     pl.Tm = take(ch * 64 * 64 * 4);
-    pl.WT = take(ch * DK * 64 * pl.esz);
-    pl.PsT = take(ch * 64 * 64 * pl.esz);
-    pl.QgsT = take(ch * DK * 64 * pl.esz);
-    pl.dhs = take(ch * DK * DV * pl.esz);
-    pl.dD = take(ch * 64 * DV * pl.esz);
+    pl.WTf = take(ch * DK * 64 * e);
+    pl.PsTf = take(ch * 64 * 64 * e);
+    pl.QgsTf = take(ch * DK * 64 * e);
+    pl.Ktf = take(ch * 64 * DK * e);
+    pl.dOf = take(ch * DV * 64 * e);
+    pl.dhs = take(ch * DK * DV * e);
+    pl.dD = take(ch * 64 * DV * e);
   }
   pl.total = o + 256;  // slack for base alignment
   return pl;
@@ -131,8 +138,10 @@ gdr::Geo make_geo(const gdr_problem* p, const Plan& pl, const int32_t* cu, char*
 }
 
 // DV tile of the serial scans: the largest of 64 / 32 / 16 that still gives
-// at least two workgroups per compute unit (512), else 16.
-int pick_dvt(int units, int dv) {
+// at least two workgroups per compute unit (512), else 16.  The fp32 path
+// always uses 16 (its operand fragments are 8x larger per k).
+int pick_dvt(int units, int dv, bool f32) {
+  if (f32) return 16;
   if ((long)units * (dv / 64) >= 512) return 64;
   if ((long)units * (dv / 32) >= 512) return 32;
   return 16;
@@ -214,20 +223,15 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, con
     gdr::WyArgs wa{};
     wa.geo = geo; wa.DV = p->dv; wa.scale = scale;
     wa.q = q; wa.k = k; wa.v = v; wa.beta = beta; wa.g = g;
-    wa.gam = (float*)(ws + pl.gam); wa.W = ws + pl.W; wa.KtT = ws + pl.KtT; wa.UT = ws + pl.UT;
+    wa.gam = (float*)(ws + pl.gam); wa.Wf = ws + pl.Wf; wa.KtTf = ws + pl.KtTf; wa.Ua = ws + pl.Ua;
+    wa.Qgf = ws + pl.Qgf; wa.Pf = ws + pl.Pf;
     GDR_LAUNCH(GDR_KERNEL_WY, s, gdr::launch_wy(wa, pl.f32, p->dk, false, s));
   }
   gdr::ScanFwdArgs sa{};
-  sa.geo = geo; sa.DV = p->dv; sa.layout = p->layout; sa.h0 = h0; sa.hT = hT;
-  sa.gam = (const float*)(ws + pl.gam); sa.W = ws + pl.W; sa.KtT = ws + pl.KtT; sa.UT = ws + pl.UT;
-  sa.hs = hs; sa.Dt = ws + pl.Dt;
-  GDR_LAUNCH(GDR_KERNEL_SCAN_FWD, s, gdr::launch_scan_fwd(sa, pl.f32, p->h_store_dtype, p->dk, pick_dvt(pl.N * p->heads, p->dv), s));
-  if (pl.NCb > 0) {
-    gdr::OutArgs oa{};
-    oa.geo = geo; oa.DV = p->dv; oa.scale = scale; oa.q = q; oa.k = k;
-    oa.gam = (const float*)(ws + pl.gam); oa.hs = hs; oa.Dt = ws + pl.Dt; oa.o = o;
-    GDR_LAUNCH(GDR_KERNEL_OUT, s, gdr::launch_out(oa, pl.f32, p->h_store_dtype, p->dk, s));
-  }
+  sa.geo = geo; sa.DV = p->dv; sa.layout = p->layout; sa.scale = scale; sa.h0 = h0; sa.hT = hT;
+  sa.gam = (const float*)(ws + pl.gam); sa.Wf = ws + pl.Wf; sa.KtTf = ws + pl.KtTf; sa.Ua = ws + pl.Ua;
+  sa.Qgf = ws + pl.Qgf; sa.Pf = ws + pl.Pf; sa.o = o; sa.hs = hs;
+  GDR_LAUNCH(GDR_KERNEL_SCAN_FWD, s, gdr::launch_scan_fwd(sa, pl.f32, p->h_store_dtype, p->dk, pick_dvt(pl.N * p->heads, p->dv, pl.f32), s));
   return GDR_OK;
 }
 
@@ -258,35 +262,37 @@ gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, con
   const float scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->dk);
   gdr::Geo geo = make_geo(p, pl, cu_seqlens, ws);
   const void* hs = h_saved ? h_saved : (const void*)(ws + pl.hs);
-  const int dvt = pick_dvt(pl.N * p->heads, p->dv);
+  const int dvt = pick_dvt(pl.N * p->heads, p->dv, pl.f32);
 
   if (p->varlen)
     GDR_LAUNCH(GDR_KERNEL_PLAN, s, gdr::launch_plan(cu_seqlens, pl.N, p->seqlen, pl.NCb, (int*)(ws + pl.seq_chunk), (int*)(ws + pl.chunk_seq), s));
   if (pl.NCb > 0) {
     gdr::WyArgs wa{};
     wa.geo = geo; wa.DV = p->dv; wa.scale = scale;
-    wa.q = q; wa.k = k; wa.v = v; wa.beta = beta; wa.g = g;
-    wa.gam = (float*)(ws + pl.gam); wa.W = ws + pl.W; wa.KtT = ws + pl.KtT; wa.UT = ws + pl.UT;
-    wa.Tm = (float*)(ws + pl.Tm); wa.WT = ws + pl.WT; wa.PsT = ws + pl.PsT; wa.QgsT = ws + pl.QgsT;
+    wa.q = q; wa.k = k; wa.v = v; wa.dO = dO; wa.beta = beta; wa.g = g;
+    wa.gam = (float*)(ws + pl.gam); wa.Wf = ws + pl.Wf; wa.Ua = ws + pl.Ua;
+    wa.KtTf = h_saved ? nullptr : (void*)(ws + pl.KtTf);
+    wa.Tm = (float*)(ws + pl.Tm); wa.WTf = ws + pl.WTf; wa.PsTf = ws + pl.PsTf; wa.QgsTf = ws + pl.QgsTf;
+    wa.Ktf = ws + pl.Ktf; wa.dOf = ws + pl.dOf;
     GDR_LAUNCH(GDR_KERNEL_WY, s, gdr::launch_wy(wa, pl.f32, p->dk, true, s));
     if (!h_saved) {
       gdr::ScanFwdArgs sa{};
-      sa.geo = geo; sa.DV = p->dv; sa.layout = p->layout; sa.h0 = h0; sa.hT = nullptr;
-      sa.gam = (const float*)(ws + pl.gam); sa.W = ws + pl.W; sa.KtT = ws + pl.KtT; sa.UT = ws + pl.UT;
-      sa.hs = ws + pl.hs; sa.Dt = nullptr;
+      sa.geo = geo; sa.DV = p->dv; sa.layout = p->layout; sa.scale = scale; sa.h0 = h0; sa.hT = nullptr;
+      sa.gam = (const float*)(ws + pl.gam); sa.Wf = ws + pl.Wf; sa.KtTf = ws + pl.KtTf; sa.Ua = ws + pl.Ua;
+      sa.Qgf = nullptr; sa.Pf = nullptr; sa.o = nullptr; sa.hs = ws + pl.hs;
       GDR_LAUNCH(GDR_KERNEL_SCAN_FWD, s, gdr::launch_scan_fwd(sa, pl.f32, p->h_store_dtype, p->dk, dvt, s));
     }
   }
   gdr::ScanBwdArgs ba{};
   ba.geo = geo; ba.DV = p->dv; ba.layout = p->layout; ba.dhT = dhT; ba.dh0 = dh0;
-  ba.k = k; ba.dO = dO; ba.gam = (const float*)(ws + pl.gam); ba.PsT = ws + pl.PsT; ba.QgsT = ws + pl.QgsT;
-  ba.WT = ws + pl.WT; ba.dhs = ws + pl.dhs; ba.dD = ws + pl.dD;
+  ba.gam = (const float*)(ws + pl.gam); ba.Ktf = ws + pl.Ktf; ba.PsTf = ws + pl.PsTf; ba.QgsTf = ws + pl.QgsTf;
+  ba.WTf = ws + pl.WTf; ba.dOf = ws + pl.dOf; ba.dhs = ws + pl.dhs; ba.dD = ws + pl.dD;
   GDR_LAUNCH(GDR_KERNEL_SCAN_BWD, s, gdr::launch_scan_bwd(ba, pl.f32, p->dk, dvt, s));
   if (pl.NCb > 0) {
     gdr::GradArgs ga{};
     ga.geo = geo; ga.DV = p->dv; ga.scale = scale;
     ga.q = q; ga.k = k; ga.v = v; ga.dO = dO; ga.beta = beta;
-    ga.gam = (const float*)(ws + pl.gam); ga.W = ws + pl.W; ga.UT = ws + pl.UT; ga.Tm = (const float*)(ws + pl.Tm);
+    ga.gam = (const float*)(ws + pl.gam); ga.Wf = ws + pl.Wf; ga.Ua = ws + pl.Ua; ga.Tm = (const float*)(ws + pl.Tm);
     ga.hs = hs; ga.dhs = ws + pl.dhs; ga.dD = ws + pl.dD;
     ga.dq = dq; ga.dk = dk; ga.dv = dv; ga.dbeta = dbeta; ga.dg = dg;
     GDR_LAUNCH(GDR_KERNEL_GRAD, s, gdr::launch_grad(ga, pl.f32, p->h_store_dtype, p->dk, s));

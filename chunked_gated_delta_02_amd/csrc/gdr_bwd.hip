@@ -33,18 +33,29 @@
 namespace gdr {
 
 // ---------------------------------------------------------------------------
+// k_scan_bwd: per (sequence, head, DV tile), chunks last to first.  dh (the
+// gradient of the state at the chunk's end, DK x DVT fp32) lives in MFMA
+// accumulators; a bf16 copy dh^T in LDS is the B operand of K dh.  The
+// per-chunk operands that do not depend on dh (E K, scale P^T, scale Qg^T,
+// W^T, dO^T, e^{gamma_L}), all in fragment order, are loaded raw into a ring
+// of SCAN_STAGES register sets, SCAN_STAGES - 1 chunks ahead.  Writes the dh
+// snapshot and dDelta (accumulator order) and dh0.
+#define SCAN_STAGES 3
+
 template <typename T, int DK, int DVT>
 __global__ __launch_bounds__(256) void k_scan_bwd(const ScanBwdArgs a) {
   constexpr int P = pad_of<T>();
   constexpr int LDH = DK + P;
   constexpr int LDD = 64 + P;
-  constexpr int LDO = DVT + P;
   constexpr int KW = Mma<T>::KW;
+  constexpr int KS = DK / KW;
+  constexpr int KS64 = 64 / KW;
   constexpr int MTH = DK / 64;
   constexpr int NT = DVT / 16;
-  __shared__ __align__(16) T sDH[DVT * LDH];  // dh^T (dv, dk), operand copy
-  __shared__ __align__(16) T sDO[64 * LDO];   // dO rows (r, dv)
-  __shared__ __align__(16) T sDD[DVT * LDD];  // dDelta^T (dv, r)
+  constexpr int S = sizeof(T) == 2 ? SCAN_STAGES : 2;  // fp32 fragments are 8x larger
+  typedef typename Mma<T>::frag frag;
+  __shared__ __align__(16) T sDH[DVT * LDH];     // dh^T (dv, dk), operand copy
+  __shared__ __align__(16) T sDD[DVT * LDD];     // -dDelta^T (dv, r)
 
   const int H = a.geo.H, DV = a.DV;
   const int Pn = a.geo.N * H;
@@ -56,8 +67,8 @@ __global__ __launch_bounds__(256) void k_scan_bwd(const ScanBwdArgs a) {
   seq_range(a.geo, n, c0, nc, ts, tl);
   const int w = wave_id();
   const int dkw = w * (DK / 4);
-  const T* kp = (const T*)a.k;
-  const T* dop = (const T*)a.dO;
+  const int rw = 16 * w;
+  const int64_t chb = (int64_t)h * a.geo.nchunks + c0;
 
   f32x4 acc_h[MTH][NT];
   const int64_t sb = (int64_t)(n * H + h) * DK * DV;
@@ -77,86 +88,113 @@ __global__ __launch_bounds__(256) void k_scan_bwd(const ScanBwdArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) store_acc_t(sDH, LDH, dkw + 16 * mt, 16 * nt, acc_h[mt][nt]);
 
-  for (int c = nc - 1; c >= 0; --c) {
-    const int ci = c0 + c;
-    const int64_t ch = (int64_t)ci * H + h;
-    const int t0 = ts + c * CH;
-    const int len = min(CH, tl - c * CH);
+  struct Ops {
+    frag kf[KS];           // E K rows 16w (rows >= len are zero)
+    frag pf[KS64];         // scale P^T rows 16w
+    frag qf[MTH][KS64];    // scale Qg^T rows dkw..
+    frag wf[MTH][KS64];    // W^T rows dkw..
+    frag dof[NT][KS64];    // dO^T rows dv (B operand: k = chunk row, j = dv)
+    float eL;              // e^{gamma_L}
+  };
+  auto load_ops = [&](int c, Ops& o) {
+    const int64_t ch = chb + c;
+    const T* Kb = (const T*)a.Ktf + ch * 64 * DK;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) o.kf[ks] = frag_af<T, DK>(Kb, w, ks);
+    const T* Pb = (const T*)a.PsTf + ch * 4096;
+#pragma unroll
+    for (int ks = 0; ks < KS64; ++ks) o.pf[ks] = frag_af<T, 64>(Pb, w, ks);
+    const T* Qb = (const T*)a.QgsTf + ch * DK * 64;
+    const T* Wb = (const T*)a.WTf + ch * DK * 64;
+#pragma unroll
+    for (int mt = 0; mt < MTH; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < KS64; ++ks) {
+        o.qf[mt][ks] = frag_af<T, 64>(Qb, dkw / 16 + mt, ks);
+        o.wf[mt][ks] = frag_af<T, 64>(Wb, dkw / 16 + mt, ks);
+      }
+    const T* Db = (const T*)a.dOf + ch * DV * 64;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < KS64; ++ks) o.dof[nt][ks] = frag_af<T, 64>(Db, dv0 / 16 + nt, ks);
+    o.eL = a.gam[ch * GSTRIDE + 64 + 63];
+  };
+
+  auto process = [&](int c, Ops& o) {
+    const int64_t ch = chb + c;
     {
-      T* db = (T*)a.dhs + ch * DK * DV + dv0;
+      T* db = (T*)a.dhs + ch * DK * DV;
 #pragma unroll
       for (int mt = 0; mt < MTH; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) store_acc(db, DV, dkw + 16 * mt, 16 * nt, acc_h[mt][nt]);
+        for (int nt = 0; nt < NT; ++nt) store_acc4(db + acc_off(dkw / 16 + mt, dv0 / 16 + nt, DV), acc_h[mt][nt]);
     }
-    __syncthreads();  // previous chunk's readers of sDO / sDD are done
-    load_rows<T, DVT>(sDO, LDO, dop + ((int64_t)t0 * H + h) * DV + dv0, (int64_t)H * DV, len);
     __syncthreads();
-    const float gL = a.gam[ch * 64 + 63];
-    // dDelta = E (K dh) + scale P^T dO, rows 16w
+    // dDelta = (E K) dh + scale P^T dO, rows 16w
     f32x4 acc_d[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc_d[nt] = zero4();
-    const T* kb = kp + ((int64_t)t0 * H + h) * DK;
 #pragma unroll
-    for (int ks = 0; ks < DK; ks += KW) {
-      const auto af = frag_rowk_masked(kb, (int64_t)H * DK, 16 * w, ks, len);
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc_d[nt] = Mma<T>::mma(af, frag_rowk(sDH, LDH, 16 * nt, ks), acc_d[nt]);
-    }
+      for (int nt = 0; nt < NT; ++nt) acc_d[nt] = Mma<T>::mma(o.kf[ks], frag_rowk(sDH, LDH, 16 * nt, ks * KW), acc_d[nt]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float E = expf(gL - a.gam[ch * 64 + 16 * w + acc_row0() + i]);
+    for (int ks = 0; ks < KS64; ++ks)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc_d[nt][i] *= E;
-    }
-    const T* Pb = (const T*)a.PsT + ch * 4096;
-#pragma unroll
-    for (int ks = 0; ks < 64; ks += KW) {
-      const auto af = frag_rowk(Pb, 64, 16 * w, ks);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc_d[nt] = Mma<T>::mma(af, frag_colk_lds(sDO, LDO, 16 * nt, ks), acc_d[nt]);
-    }
+      for (int nt = 0; nt < NT; ++nt) acc_d[nt] = Mma<T>::mma(o.pf[ks], o.dof[nt][ks], acc_d[nt]);
     {
-      T* ddb = (T*)a.dD + ch * 64 * DV + dv0;
+      T* ddb = (T*)a.dD + ch * 64 * DV;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        store_acc_t(sDD, LDD, 16 * w, 16 * nt, acc_d[nt]);
-        store_acc(ddb, DV, 16 * w, 16 * nt, acc_d[nt]);
+        store_acc4(ddb + acc_off(w, dv0 / 16 + nt, DV), acc_d[nt]);
+        store_acc_t(sDD, LDD, rw, 16 * nt, -acc_d[nt]);
       }
     }
     __syncthreads();
     // dh <- e^{gamma_L} dh + (scale Qg)^T dO - W^T dDelta
-    const float eL = expf(gL);
 #pragma unroll
     for (int mt = 0; mt < MTH; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc_h[mt][nt] *= eL;
-    const T* Qb = (const T*)a.QgsT + ch * DK * 64;
-    const T* Wb = (const T*)a.WT + ch * DK * 64;
+      for (int nt = 0; nt < NT; ++nt) acc_h[mt][nt] *= o.eL;
 #pragma unroll
-    for (int ks = 0; ks < 64; ks += KW) {
-      typename Mma<T>::frag aq[MTH], aw[MTH];
-#pragma unroll
-      for (int mt = 0; mt < MTH; ++mt) {
-        aq[mt] = frag_rowk(Qb, 64, dkw + 16 * mt, ks);
-        aw[mt] = Mma<T>::neg(frag_rowk(Wb, 64, dkw + 16 * mt, ks));
-      }
+    for (int ks = 0; ks < KS64; ++ks)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const auto bo = frag_colk_lds(sDO, LDO, 16 * nt, ks);
-        const auto bd = frag_rowk(sDD, LDD, 16 * nt, ks);
+        const frag bo = o.dof[nt][ks];
+        const frag bd = frag_rowk(sDD, LDD, 16 * nt, ks * KW);
 #pragma unroll
         for (int mt = 0; mt < MTH; ++mt) {
-          acc_h[mt][nt] = Mma<T>::mma(aq[mt], bo, acc_h[mt][nt]);
-          acc_h[mt][nt] = Mma<T>::mma(aw[mt], bd, acc_h[mt][nt]);
+          acc_h[mt][nt] = Mma<T>::mma(o.qf[mt][ks], bo, acc_h[mt][nt]);
+          acc_h[mt][nt] = Mma<T>::mma(o.wf[mt][ks], bd, acc_h[mt][nt]);
         }
       }
-    }
 #pragma unroll
     for (int mt = 0; mt < MTH; ++mt)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) store_acc_t(sDH, LDH, dkw + 16 * mt, 16 * nt, acc_h[mt][nt]);
+  };
+
+  // Chunks are processed last to first: step j handles chunk nc - 1 - j and
+  // lives in register stage j % S.  As in the forward scan, the main loop
+  // runs S steps per trip with unconditional prefetches (index clamped to
+  // the first chunk) so the prefetched loads stay in flight, and a static
+  // tail runs the last nc % S steps.
+  if (nc > 0) {
+    Ops st[S];
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s) load_ops(nc - 1 - min(s, nc - 1), st[s]);
+    int jb = 0;
+    for (; jb + S <= nc; jb += S) {
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        load_ops(nc - 1 - min(jb + s + S - 1, nc - 1), st[(s + S - 1) % S]);
+        process(nc - 1 - (jb + s), st[s]);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s)
+      if (jb + s < nc) process(nc - 1 - (jb + s), st[s]);
   }
   if (a.dh0) {
 #pragma unroll
@@ -190,7 +228,7 @@ __global__ __launch_bounds__(256) void k_grad(const GradArgs a) {
   constexpr int NTK = DK / 16;
   constexpr int NTB = DVB / 16;
   typedef typename Mma<T>::frag frag;
-  constexpr int PH1 = (DVB * LDK + DK * LDV + DVB * L64 + 2 * 64 * LDV) * (int)sizeof(T);
+  constexpr int PH1 = (2 * DVB * LDK + 2 * DVB * L64 + 64 * LDV) * (int)sizeof(T);
   constexpr int PH2 = (2 * 64 * LDK + DK * L64 + 64 * L64) * (int)sizeof(T);
   extern __shared__ __align__(16) char smem[];
   T* sT = (T*)smem;                       // T (r, s), operand copy
@@ -203,10 +241,10 @@ __global__ __launch_bounds__(256) void k_grad(const GradArgs a) {
   char* uni = (char*)(sMisc + 8);
   // phase 1
   T* sHvk = (T*)uni;                      // h rows (dv, dk)
-  T* sDHkv = sHvk + DVB * LDK;            // dh (dk, dv)
-  T* sDeltaT = sDHkv + DK * LDV;          // Delta^T (dv, r)
-  T* sDD = sDeltaT + DVB * L64;           // dDelta (r, dv)
-  T* sV = sDD + 64 * LDV;                 // V (r, dv)
+  T* sDHvk = sHvk + DVB * LDK;            // dh rows (dv, dk)
+  T* sDeltaT = sDHvk + DVB * LDK;         // Delta^T (dv, r)
+  T* sDDt = sDeltaT + DVB * L64;          // dDelta^T (dv, r)
+  T* sV = sDDt + DVB * L64;               // V (r, dv)
   // phase 2 (aliases phase 1)
   T* sQ = (T*)uni;                        // Q (r, dk); later dT^T (s, r)
   T* sK = sQ + 64 * LDK;                  // K (r, dk)
@@ -219,7 +257,7 @@ __global__ __launch_bounds__(256) void k_grad(const GradArgs a) {
   if (!chunk_lookup(a.geo, ci, n, t0, len)) return;
   const int H = a.geo.H, DV = a.DV;
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
-  const int64_t ch = (int64_t)ci * H + h;
+  const int64_t ch = (int64_t)h * a.geo.nchunks + ci;
   const T* qp = (const T*)a.q;
   const T* kp = (const T*)a.k;
   const T* vp = (const T*)a.v;
@@ -227,12 +265,10 @@ __global__ __launch_bounds__(256) void k_grad(const GradArgs a) {
   const float scale = a.scale;
 
   if (tid < 64) {
-    const float gm = a.gam[ch * 64 + tid];
-    const float gL = a.gam[ch * 64 + 63];
-    sg[tid] = gm;
+    sg[tid] = a.gam[ch * GSTRIDE + tid];
     sb[tid] = (tid < len) ? a.beta[(int64_t)(t0 + tid) * H + h] : 0.f;
-    seg[tid] = expf(gm);
-    sE[tid] = expf(gL - gm);
+    seg[tid] = a.gam[ch * GSTRIDE + 64 + tid];
+    sE[tid] = a.gam[ch * GSTRIDE + 128 + tid];
   }
   for (int e = tid; e < 64 * 64; e += 256) sT[(e >> 6) * L64 + (e & 63)] = from_f32<T>(a.Tm[ch * 4096 + e]);
   const int rw = 16 * w;            // first output row of this wave
@@ -247,9 +283,9 @@ __global__ __launch_bounds__(256) void k_grad(const GradArgs a) {
   // W fragments for Delta = U - W h (rows 16w), negated
   frag wf[DK / KW];
   {
-    const T* Wb = (const T*)a.W + ch * 64 * DK;
+    const T* Wb = (const T*)a.Wf + ch * 64 * DK;
 #pragma unroll
-    for (int ks = 0; ks < DK / KW; ++ks) wf[ks] = Mma<T>::neg(frag_rowk(Wb, DK, rw, ks * KW));
+    for (int ks = 0; ks < DK / KW; ++ks) wf[ks] = Mma<T>::neg(frag_af<T, DK>(Wb, w, ks));
   }
   f32x4 aQ[NTK], aKt[NTK], aW[NTK], aP[4], aTV[4];
 #pragma unroll
@@ -260,25 +296,39 @@ __global__ __launch_bounds__(256) void k_grad(const GradArgs a) {
   const int64_t rowq = (int64_t)t0 * H + h;   // token-row index of chunk row 0
   for (int dvb = 0; dvb < DV; dvb += DVB) {
     __syncthreads();
-    load_rows_conv<HS, T, DK, DVB>(sHvk, LDK, (const HS*)a.hs + (ch * DV + dvb) * DK, DK, DVB);
-    load_rows<T, DVB, DK>(sDHkv, LDV, (const T*)a.dhs + ch * DK * DV + dvb, DV, DK);
-    load_rows<T, DVB>(sDD, LDV, (const T*)a.dD + ch * 64 * DV + dvb, DV, 64);
-    load_rows<T, DVB>(sV, LDV, vp + rowq * DV + dvb, (int64_t)H * DV, len);
-    __syncthreads();
-    // e^{gamma_L} <dh, h>: h from the snapshot in its stored precision
+    // h and dh (accumulator order <DK, DV>) and dDelta (accumulator order
+    // <64, DV>) of this DV block, transposed into (dv, .) rows in LDS;
+    // <dh, h> (for e^{gamma_L} <dh, h>) uses h in its stored precision
     {
-      const HS* hb = (const HS*)a.hs + (ch * DV + dvb) * DK;
-      for (int e = tid; e < DVB * DK; e += 256) {
-        const int dvl = e / DK, dk = e - dvl * DK;
-        gLh += to_f32(hb[e]) * to_f32(sDHkv[dk * LDV + dvl]);
+      const HS* hb = (const HS*)a.hs + ch * DK * DV;
+      const T* db = (const T*)a.dhs + ch * DK * DV;
+      for (int e = tid; e < (DK / 16) * NTB * 64; e += 256) {
+        const int ll = e & 63, tt = e >> 6;
+        const int m = tt / NTB, nn = tt - m * NTB;
+        const int64_t off = acc_off_l(m, dvb / 16 + nn, DV, ll);
+        const int dk = 16 * m + 4 * (ll >> 4), dvl = 16 * nn + (ll & 15);
+        const f32x4 hv = load4f(hb + off);
+        const f32x4 gv = load4f(db + off);
+        gLh += hv[0] * gv[0] + hv[1] * gv[1] + hv[2] * gv[2] + hv[3] * gv[3];
+        store_acc4(sHvk + dvl * LDK + dk, hv);
+        store_acc4(sDHvk + dvl * LDK + dk, gv);
+      }
+      const T* ddb = (const T*)a.dD + ch * 64 * DV;
+      for (int e = tid; e < 4 * NTB * 64; e += 256) {
+        const int ll = e & 63, tt = e >> 6;
+        const int m = tt / NTB, nn = tt - m * NTB;
+        const int r = 16 * m + 4 * (ll >> 4), dvl = 16 * nn + (ll & 15);
+        store_acc4(sDDt + dvl * L64 + r, load4f(ddb + acc_off_l(m, dvb / 16 + nn, DV, ll)));
       }
     }
+    load_rows<T, DVB>(sV, LDV, vp + rowq * DV + dvb, (int64_t)H * DV, len);
+    __syncthreads();
     // Delta block = U - W h  (rows 16w)
     f32x4 aD[NTB];
     {
-      const T* Ub = (const T*)a.UT + (ch * DV + dvb) * 64;
+      const T* Ub = (const T*)a.Ua + ch * 64 * DV;
 #pragma unroll
-      for (int nt = 0; nt < NTB; ++nt) aD[nt] = load4f(Ub + (16 * nt + acc_col()) * 64 + r0);
+      for (int nt = 0; nt < NTB; ++nt) aD[nt] = load4f(Ub + acc_off(w, dvb / 16 + nt, DV));
 #pragma unroll
       for (int ks = 0; ks < DK / KW; ++ks)
 #pragma unroll
@@ -295,7 +345,7 @@ __global__ __launch_bounds__(256) void k_grad(const GradArgs a) {
     // dQg += dO h^T ; dW -= dDelta h^T ; dT_V += dDelta V^T
 #pragma unroll
     for (int ks = 0; ks < DVB / KW; ++ks) {
-      const frag ddp = frag_rowk(sDD, LDV, rw, ks * KW);
+      const frag ddp = frag_colk_lds(sDDt, L64, rw, ks * KW);
       const frag ddn = Mma<T>::neg(ddp);
 #pragma unroll
       for (int nt = 0; nt < NTK; ++nt) {
@@ -312,7 +362,7 @@ __global__ __launch_bounds__(256) void k_grad(const GradArgs a) {
     for (int ks = 0; ks < DVB / KW; ++ks) {
       const frag ad = frag_colk_lds(sDeltaT, L64, rw, ks * KW);
 #pragma unroll
-      for (int nt = 0; nt < NTK; ++nt) aKt[nt] = Mma<T>::mma(ad, frag_rowk(sDHkv, LDV, 16 * nt, ks * KW), aKt[nt]);
+      for (int nt = 0; nt < NTK; ++nt) aKt[nt] = Mma<T>::mma(ad, frag_colk_lds(sDHvk, LDK, 16 * nt, ks * KW), aKt[nt]);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) aP[nt] = Mma<T>::mma(dof[ks], frag_colk_lds(sDeltaT, L64, 16 * nt, ks * KW), aP[nt]);
     }
@@ -325,7 +375,7 @@ __global__ __launch_bounds__(256) void k_grad(const GradArgs a) {
       for (int ks = 0; ks < 64; ks += KW) {
         const frag at = frag_colk_lds(sT, L64, rw, ks);
 #pragma unroll
-        for (int nt = 0; nt < NTB; ++nt) aVb[nt] = Mma<T>::mma(at, frag_colk_lds(sDD, LDV, 16 * nt, ks), aVb[nt]);
+        for (int nt = 0; nt < NTB; ++nt) aVb[nt] = Mma<T>::mma(at, frag_rowk(sDDt, L64, 16 * nt, ks), aVb[nt]);
       }
       T* dvp = (T*)a.dv;
 #pragma unroll
@@ -630,7 +680,7 @@ template <typename T, int DK>
 static size_t grad_smem() {
   constexpr int P = pad_of<T>();
   constexpr int LDK = DK + P, L64 = 64 + P, DVB = dvb_of<T>(), LDV = DVB + P;
-  constexpr int PH1 = (DVB * LDK + DK * LDV + DVB * L64 + 2 * 64 * LDV) * (int)sizeof(T);
+  constexpr int PH1 = (2 * DVB * LDK + 2 * DVB * L64 + 64 * LDV) * (int)sizeof(T);
   constexpr int PH2 = (2 * 64 * LDK + DK * L64 + 64 * L64) * (int)sizeof(T);
   return 64 * L64 * sizeof(T) + (4 * 64 + 2 * 4 * 64 + 8) * 4 + cmax(PH1, PH2);
 }

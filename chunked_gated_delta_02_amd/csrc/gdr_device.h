@@ -131,6 +131,33 @@ __device__ __forceinline__ typename Mma<T>::frag frag_colk_lds(const T* p, int l
 }
 
 // ---------------------------------------------------------------------------
+// Fragment order ("afrag"): an R x K operand matrix (rows i, contraction
+// index k) stored so that the fragment of row tile m and k-step s -- what
+// one wave feeds to one MFMA -- is 64 lanes x KPL contiguous elements.  A
+// wave loads a fragment with one fully coalesced access (1 KB for bf16).
+template <typename T, int K>
+__device__ __forceinline__ int64_t afrag_off(int i, int k) {
+  constexpr int KW = Mma<T>::KW, KPL = Mma<T>::KPL;
+  const int lane = (i & 15) + 16 * ((k % KW) / KPL);
+  return ((int64_t)((i >> 4) * (K / KW) + k / KW) * 64 + lane) * KPL + (k % KPL);
+}
+template <typename T, int K>
+__device__ __forceinline__ typename Mma<T>::frag frag_af(const T* p, int m, int s) {
+  const T* q = p + ((int64_t)(m * (K / Mma<T>::KW) + s) * 64 + lane_id()) * Mma<T>::KPL;
+  return *reinterpret_cast<const typename Mma<T>::frag*>(q);
+}
+
+// Accumulator order ("acc"): an R x C matrix stored so that 16 x 16 tile
+// (m, n) is 64 lanes x 4 contiguous elements in the MFMA result layout
+// (lane l holds rows 16m + 4(l>>4) + i, column 16n + (l&15)).
+__device__ __forceinline__ int64_t acc_off(int m, int n, int C) {
+  return ((int64_t)(m * (C / 16) + n) * 64 + lane_id()) * 4;
+}
+__device__ __forceinline__ int64_t acc_off_l(int m, int n, int C, int l) {
+  return ((int64_t)(m * (C / 16) + n) * 64 + l) * 4;
+}
+
+// ---------------------------------------------------------------------------
 // Accumulator tile element map: lane l holds C[r0 + i][c], i < 4, with
 // r0 = 4*(l>>4), c = l & 15 (relative to the tile origin).
 __device__ __forceinline__ int acc_row0() { return 4 * (lane_id() >> 4); }
@@ -141,6 +168,19 @@ __device__ __forceinline__ int acc_col() { return lane_id() & 15; }
 template <typename T>
 __device__ __forceinline__ void store_acc_t(T* dst, int ld, int r0, int c0, f32x4 v) {
   T* q = dst + (int64_t)(c0 + acc_col()) * ld + r0 + acc_row0();
+  if constexpr (sizeof(T) == 2) {
+    typedef T t4 __attribute__((ext_vector_type(4)));
+    t4 w = {(T)v[0], (T)v[1], (T)v[2], (T)v[3]};
+    *reinterpret_cast<t4*>(q) = w;
+  } else {
+    *reinterpret_cast<f32x4*>(q) = v;
+  }
+}
+
+// Store / load an accumulator tile in accumulator order (4 contiguous
+// elements per lane: 8-byte or 16-byte accesses, 64 lanes contiguous).
+template <typename T>
+__device__ __forceinline__ void store_acc4(T* q, f32x4 v) {
   if constexpr (sizeof(T) == 2) {
     typedef T t4 __attribute__((ext_vector_type(4)));
     t4 w = {(T)v[0], (T)v[1], (T)v[2], (T)v[3]};

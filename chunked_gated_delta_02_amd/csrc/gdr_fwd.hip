@@ -21,8 +21,7 @@
 //   k_wy        chunk-parallel: gamma, T, W, U (and backward extras)
 //   k_scan_fwd  serial over chunks per (sequence, head, DV tile): the state
 //               tile lives in registers (fp32 MFMA accumulators) with a bf16
-//               copy in LDS; writes per-chunk snapshots, Delta and h_T
-//   k_out       chunk-parallel: O
+//               copy in LDS; writes per-chunk snapshots, o and h_T
 #include "gdr_kernels.h"
 
 namespace gdr {
@@ -91,11 +90,10 @@ __global__ __launch_bounds__(1024) void k_plan(const int* cu, int N, int T_total
 // ---------------------------------------------------------------------------
 // k_wy: per (chunk, head).  Computes gamma, A, T = (I + A)^-1 (blocked:
 // 16 x 16 diagonal blocks by forward substitution, then off-diagonal block
-// rows T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj on fp32 MFMA), then W and U on
-// the operand-type MFMA.  Workspace outputs (chunk-major, [slot][head][..]):
-//   gam [64] fp32, W [64][DK], KtT [DK][64] = (diag(e^{gL-g}) K)^T,
-//   UT [DV][64] = U^T; with BWD also Tm [64][64] fp32, WT [DK][64],
-//   PsT [64][64] = (scale (Q K^T * Gam))^T, QgsT [DK][64] = (scale e^g Q)^T.
+// rows T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj on fp32 MFMA), W and U on the
+// operand-type MFMA, and P = Q K^T * Gam; writes everything the scans and
+// the gradient kernel consume, in fragment / accumulator order (see
+// gdr_kernels.h).
 template <typename T, int DK, bool BWD>
 __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
   constexpr int P = pad_of<T>();
@@ -105,14 +103,18 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
   constexpr int DVB = dvb_of<T>();
   constexpr int LDV = DVB + P;
   constexpr int KW = Mma<T>::KW;
-  constexpr int UNION = cmax(cmax(64 * LDF * 4, 64 * LDV * (int)sizeof(T)),
-                             BWD ? 64 * LDK * (int)sizeof(T) : 0);
+  constexpr int R1 = cmax(cmax(2 * 64 * LDF * 4, (64 * LDK + 64 * LDV) * (int)sizeof(T)),
+                          (64 * LDK + 64 * L64) * (int)sizeof(T));
   extern __shared__ __align__(16) char smem[];
   T* sK = (T*)smem;
-  char* uni = smem + 64 * LDK * sizeof(T);
-  float* sA = (float*)uni;
-  float* sTm = (float*)(uni + UNION);
-  T* sT1 = (T*)(sTm + 64 * LDF);
+  char* r1 = smem + 64 * LDK * sizeof(T);
+  float* sA = (float*)r1;              // A (fp32), then dead
+  float* sTm = sA + 64 * LDF;          // T (fp32), then dead
+  T* sW = (T*)r1;                      // W (r, dk), after T1/T2 are built
+  T* sV = sW + 64 * LDK;               // V / dO block (r, dv)
+  T* sQ = (T*)r1;                      // Q (r, dk), after W and V are done
+  T* sP = sQ + 64 * LDK;               // P (r, s)
+  T* sT1 = (T*)(r1 + R1);
   T* sT2 = sT1 + 64 * L64;
   float* sX = (float*)(sT2 + 64 * L64);
   float* sg = sX + 4 * 16 * 20;
@@ -125,7 +127,7 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
   if (!chunk_lookup(a.geo, ci, n, t0, len)) return;
   const int H = a.geo.H, DV = a.DV;
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
-  const int64_t ch = (int64_t)ci * H + h;
+  const int64_t ch = (int64_t)h * a.geo.nchunks + ci;
   const T* kp = (const T*)a.k;
   const T* vp = (const T*)a.v;
 
@@ -137,11 +139,14 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
     }
     const float gm = wave_incl_scan(gv);
     const float gL = __shfl(gm, 63, 64);
+    const float eg = expf(gm), eE = expf(gL - gm);
     sg[l] = gm;
     sb[l] = bv;
-    seg[l] = expf(gm);
-    sE[l] = expf(gL - gm);
-    a.gam[ch * 64 + l] = gm;
+    seg[l] = eg;
+    sE[l] = eE;
+    a.gam[ch * GSTRIDE + l] = gm;
+    a.gam[ch * GSTRIDE + 64 + l] = eg;
+    a.gam[ch * GSTRIDE + 128 + l] = eE;
   }
   load_rows<T, DK>(sK, LDK, kp + ((int64_t)t0 * H + h) * DK, (int64_t)H * DK, len);
   __syncthreads();
@@ -224,9 +229,10 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
     sT2[r * L64 + s] = from_f32<T>(t * sb[s]);
     if constexpr (BWD) a.Tm[ch * 4096 + e] = t;
   }
-  __syncthreads();
+  __syncthreads();  // sA / sTm are dead from here
 
-  // W^T = K^T T1^T (DK x 64): wave w owns dk rows [w DK/4, (w+1) DK/4)
+  // W^T = K^T T1^T (DK x 64): wave w owns dk rows [w DK/4, (w+1) DK/4);
+  // staged row-major in LDS, then written out in fragment order
   {
     constexpr int MT = DK / 64;
     f32x4 acc[MT][4];
@@ -246,29 +252,21 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
         for (int mt = 0; mt < MT; ++mt) acc[mt][nt] = Mma<T>::mma(af[mt], bf, acc[mt][nt]);
       }
     }
-    T* Wb = (T*)a.W + ch * 64 * DK;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        store_acc_t(Wb, DK, w * (DK / 4) + 16 * mt, 16 * nt, acc[mt][nt]);
-        if constexpr (BWD) store_acc((T*)a.WT + ch * DK * 64, 64, w * (DK / 4) + 16 * mt, 16 * nt, acc[mt][nt]);
-      }
+      for (int nt = 0; nt < 4; ++nt) store_acc_t(sW, LDK, w * (DK / 4) + 16 * mt, 16 * nt, acc[mt][nt]);
   }
-  // KtT[dk][r] = e^{gamma_L - gamma_r} K[r][dk]
-  {
-    T* Kb = (T*)a.KtT + ch * DK * 64;
-    for (int e = tid; e < DK * 8; e += 256) {
-      const int dk = e >> 3, r0 = (e & 7) * 8;
-      float vals[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) vals[j] = sE[r0 + j] * to_f32(sK[(r0 + j) * LDK + dk]);
-      store8<T>(Kb + dk * 64 + r0, vals);
-    }
+  __syncthreads();
+  write_afrag<T, 64, DK>((T*)a.Wf + ch * 64 * DK, [&](int i, int k) { return to_f32(sW[i * LDK + k]); });
+  if constexpr (BWD) {
+    write_afrag<T, DK, 64>((T*)a.WTf + ch * DK * 64, [&](int i, int k) { return to_f32(sW[k * LDK + i]); });
+    write_afrag<T, 64, DK>((T*)a.Ktf + ch * 64 * DK, [&](int i, int k) { return sE[i] * to_f32(sK[i * LDK + k]); });
   }
+  if (a.KtTf)
+    write_afrag<T, DK, 64>((T*)a.KtTf + ch * DK * 64, [&](int i, int k) { return sE[k] * to_f32(sK[k * LDK + i]); });
 
-  // U^T per DV block: U = T2 V, rows 16w
-  T* sV = (T*)uni;
+  // U = T2 V per DV block (rows 16w), written in accumulator order
   for (int dv0 = 0; dv0 < DV; dv0 += DVB) {
     __syncthreads();
     load_rows<T, DVB>(sV, LDV, vp + ((int64_t)t0 * H + h) * DV + dv0, (int64_t)H * DV, len);
@@ -283,44 +281,56 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
       for (int nt = 0; nt < DVB / 16; ++nt)
         acc[nt] = Mma<T>::mma(af, frag_colk_lds(sV, LDV, 16 * nt, ks), acc[nt]);
     }
-    T* Ub = (T*)a.UT + (ch * DV + dv0) * 64;
+    T* Ub = (T*)a.Ua + ch * 64 * DV;
 #pragma unroll
-    for (int nt = 0; nt < DVB / 16; ++nt) store_acc_t(Ub, 64, 16 * w, 16 * nt, acc[nt]);
+    for (int nt = 0; nt < DVB / 16; ++nt) store_acc4(Ub + acc_off(w, dv0 / 16 + nt, DV), acc[nt]);
+  }
+  if constexpr (BWD) {
+    // dO^T in fragment order, per DV block
+    const T* dop = (const T*)a.dO;
+    for (int dv0 = 0; dv0 < DV; dv0 += DVB) {
+      __syncthreads();
+      load_rows<T, DVB>(sV, LDV, dop + ((int64_t)t0 * H + h) * DV + dv0, (int64_t)H * DV, len);
+      __syncthreads();
+      write_afrag<T, DVB, 64>((T*)a.dOf + ch * DV * 64 + (int64_t)dv0 * 64,
+                              [&](int i, int k) { return to_f32(sV[k * LDV + i]); });
+    }
   }
 
-  if constexpr (BWD) {
-    __syncthreads();
-    T* sQ = (T*)uni;
-    load_rows<T, DK>(sQ, LDK, (const T*)a.q + ((int64_t)t0 * H + h) * DK, (int64_t)H * DK, len);
-    __syncthreads();
-    // scale (Q K^T * Gam), rows r = 16w; stored transposed
+  __syncthreads();  // sW / sV are dead from here
+  load_rows<T, DK>(sQ, LDK, (const T*)a.q + ((int64_t)t0 * H + h) * DK, (int64_t)H * DK, len);
+  __syncthreads();
+  // P = Q K^T * Gam (diagonal included), computed as P^T (rows s = 16w),
+  // staged row-major (r, s) in LDS
+  {
     f32x4 acc[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) acc[nt] = zero4();
 #pragma unroll
     for (int ks = 0; ks < DK; ks += KW) {
-      const auto af = frag_rowk(sQ, LDK, 16 * w, ks);
+      const auto af = frag_rowk(sK, LDK, 16 * w, ks);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[nt] = Mma<T>::mma(af, frag_rowk(sK, LDK, 16 * nt, ks), acc[nt]);
+      for (int nt = 0; nt < 4; ++nt) acc[nt] = Mma<T>::mma(af, frag_rowk(sQ, LDK, 16 * nt, ks), acc[nt]);
     }
-    T* Pb = (T*)a.PsT + ch * 4096;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + acc_row0() + i, s = 16 * nt + acc_col();
-        acc[nt][i] = (s <= r) ? a.scale * acc[nt][i] * expf(sg[r] - sg[s]) : 0.f;
+        const int s = 16 * w + acc_row0() + i, r = 16 * nt + acc_col();
+        acc[nt][i] = (s <= r) ? acc[nt][i] * expf(sg[r] - sg[s]) : 0.f;
       }
-      store_acc_t(Pb, 64, 16 * w, 16 * nt, acc[nt]);
+      store_acc_t(sP, L64, 16 * w, 16 * nt, acc[nt]);
     }
-    T* Qb = (T*)a.QgsT + ch * DK * 64;
-    for (int e = tid; e < DK * 8; e += 256) {
-      const int dk = e >> 3, r0 = (e & 7) * 8;
-      float vals[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) vals[j] = a.scale * seg[r0 + j] * to_f32(sQ[(r0 + j) * LDK + dk]);
-      store8<T>(Qb + dk * 64 + r0, vals);
-    }
+  }
+  __syncthreads();
+  if constexpr (!BWD) {
+    write_afrag<T, 64, 64>((T*)a.Pf + ch * 4096, [&](int i, int k) { return to_f32(sP[i * L64 + k]); });
+    write_afrag<T, 64, DK>((T*)a.Qgf + ch * 64 * DK, [&](int i, int k) { return seg[i] * to_f32(sQ[i * LDK + k]); });
+  } else {
+    const float sc = a.scale;
+    write_afrag<T, 64, 64>((T*)a.PsTf + ch * 4096, [&](int i, int k) { return sc * to_f32(sP[k * L64 + i]); });
+    write_afrag<T, DK, 64>((T*)a.QgsTf + ch * DK * 64,
+                           [&](int i, int k) { return sc * seg[k] * to_f32(sQ[k * LDK + i]); });
   }
 }
 
@@ -328,19 +338,33 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
 // k_scan_fwd: per (sequence, head, DV tile).  Serial over the sequence's
 // chunks.  The state tile h (DK x DVT, fp32) is held in MFMA accumulators
 // (wave w owns dk rows [w DK/4, (w+1) DK/4)); a bf16 copy h^T lives in LDS
-// as the B operand of Delta = U - W h.  Delta^T goes to LDS as the B operand
-// of the update h <- e^{gamma_L} h + Kt^T Delta.  W and Kt^T fragments are
-// read straight from the workspace into registers.
-template <typename T, typename HS, int DK, int DVT>
+// as the B operand of W h (and of Q h for the output).  Delta^T goes to LDS
+// as the B operand of the update h <- e^{gamma_L} h + Kt^T Delta and of
+// P Delta.  All per-chunk operands that do not depend on h (W, Kt^T, U, Q,
+// P, the gate exponentials) are loaded raw into a ring of SCAN_STAGES
+// register sets, SCAN_STAGES - 1 chunks ahead; nothing touches a loaded
+// value before its chunk is processed, so the loads stay in flight while
+// earlier chunks run.  With OUT the kernel also writes
+// o = scale (e^gamma Q h + P Delta).
+#define SCAN_STAGES 3
+
+template <typename T, typename HS, int DK, int DVT, bool OUT>
 __global__ __launch_bounds__(256) void k_scan_fwd(const ScanFwdArgs a) {
   constexpr int P = pad_of<T>();
   constexpr int LDH = DK + P;
   constexpr int LDD = 64 + P;
   constexpr int KW = Mma<T>::KW;
+  constexpr int KS = DK / KW;
+  constexpr int KS64 = 64 / KW;
   constexpr int MTH = DK / 64;
   constexpr int NT = DVT / 16;
+  constexpr int S = sizeof(T) == 2 ? SCAN_STAGES : 2;  // fp32 fragments are 8x larger
+  typedef typename Mma<T>::frag frag;
+  typedef T t4 __attribute__((ext_vector_type(4)));
+  constexpr int LDO = DVT + P;
   __shared__ __align__(16) T sH[DVT * LDH];
   __shared__ __align__(16) T sD[DVT * LDD];
+  __shared__ __align__(16) T sO[OUT ? 64 * LDO : 1];  // output staging (each wave: its rows)
 
   const int H = a.geo.H, DV = a.DV;
   const int Pn = a.geo.N * H;
@@ -351,7 +375,10 @@ __global__ __launch_bounds__(256) void k_scan_fwd(const ScanFwdArgs a) {
   int c0, nc, ts, tl;
   seq_range(a.geo, n, c0, nc, ts, tl);
   const int w = wave_id();
+  const int l = lane_id();
   const int dkw = w * (DK / 4);
+  const int rw = 16 * w;
+  const int64_t chb = (int64_t)h * a.geo.nchunks + c0;   // chunk-head index of chunk 0
 
   f32x4 acc_h[MTH][NT];
   const int64_t sb = (int64_t)(n * H + h) * DK * DV;
@@ -371,58 +398,129 @@ __global__ __launch_bounds__(256) void k_scan_fwd(const ScanFwdArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) store_acc_t(sH, LDH, dkw + 16 * mt, 16 * nt, acc_h[mt][nt]);
 
-  for (int c = 0; c < nc; ++c) {
-    const int64_t ch = (int64_t)(c0 + c) * H + h;
-    if (a.hs) {
-      HS* hb = (HS*)a.hs + (ch * DV + dv0) * DK;
+  struct Ops {
+    frag wf[KS];           // W rows 16w
+    frag kf[MTH][KS64];    // Kt^T rows dkw.., k = chunk row
+    t4 u[NT];              // U (accumulator order, raw)
+    frag qf[KS];           // e^gamma Q rows 16w
+    frag pf[KS64];         // P rows 16w
+    float eL;              // e^{gamma_L}
+  };
+  auto load_ops = [&](int c, Ops& o) {
+    const int64_t ch = chb + c;
+    const T* Wb = (const T*)a.Wf + ch * 64 * DK;
 #pragma unroll
-      for (int mt = 0; mt < MTH; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) store_acc_t(hb, DK, dkw + 16 * mt, 16 * nt, acc_h[mt][nt]);
-    }
-    __syncthreads();
-    // Delta = U - W h for rows 16w
-    f32x4 acc_d[NT];
-    const T* UTb = (const T*)a.UT + (ch * DV + dv0) * 64;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc_d[nt] = load4f(UTb + (16 * nt + acc_col()) * 64 + 16 * w + acc_row0());
-    const T* Wb = (const T*)a.W + ch * 64 * DK;
-#pragma unroll
-    for (int ks = 0; ks < DK; ks += KW) {
-      const auto af = Mma<T>::neg(frag_rowk(Wb, DK, 16 * w, ks));
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc_d[nt] = Mma<T>::mma(af, frag_rowk(sH, LDH, 16 * nt, ks), acc_d[nt]);
-    }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) store_acc_t(sD, LDD, 16 * w, 16 * nt, acc_d[nt]);
-    if (a.Dt) {
-      T* Db = (T*)a.Dt + (ch * DV + dv0) * 64;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) store_acc_t(Db, 64, 16 * w, 16 * nt, acc_d[nt]);
-    }
-    __syncthreads();
-    const float eL = expf(a.gam[ch * 64 + 63]);
+    for (int ks = 0; ks < KS; ++ks) o.wf[ks] = frag_af<T, DK>(Wb, w, ks);
+    const T* Kb = (const T*)a.KtTf + ch * DK * 64;
 #pragma unroll
     for (int mt = 0; mt < MTH; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc_h[mt][nt] *= eL;
-    const T* Kb = (const T*)a.KtT + ch * DK * 64;
+      for (int ks = 0; ks < KS64; ++ks) o.kf[mt][ks] = frag_af<T, 64>(Kb, dkw / 16 + mt, ks);
+    const T* Ub = (const T*)a.Ua + ch * 64 * DV;
 #pragma unroll
-    for (int ks = 0; ks < 64; ks += KW) {
-      typename Mma<T>::frag af[MTH];
+    for (int nt = 0; nt < NT; ++nt) o.u[nt] = *reinterpret_cast<const t4*>(Ub + acc_off(w, dv0 / 16 + nt, DV));
+    o.eL = a.gam[ch * GSTRIDE + 64 + 63];
+    if constexpr (OUT) {
+      const T* Qb = (const T*)a.Qgf + ch * 64 * DK;
 #pragma unroll
-      for (int mt = 0; mt < MTH; ++mt) af[mt] = frag_rowk(Kb, 64, dkw + 16 * mt, ks);
+      for (int ks = 0; ks < KS; ++ks) o.qf[ks] = frag_af<T, DK>(Qb, w, ks);
+      const T* Pb = (const T*)a.Pf + ch * 4096;
+#pragma unroll
+      for (int ks = 0; ks < KS64; ++ks) o.pf[ks] = frag_af<T, 64>(Pb, w, ks);
+    }
+  };
+
+  auto process = [&](int c, Ops& o) {
+    const int64_t ch = chb + c;
+    {
+      HS* hb = (HS*)a.hs + ch * DK * DV;
+#pragma unroll
+      for (int mt = 0; mt < MTH; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) store_acc4(hb + acc_off(dkw / 16 + mt, dv0 / 16 + nt, DV), acc_h[mt][nt]);
+    }
+    __syncthreads();  // h^T in LDS is complete; last chunk's readers of Delta^T are done
+    // W h and (with OUT) Q h, rows 16w
+    f32x4 acc_d[NT], acc_o[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc_d[nt] = acc_o[nt] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const auto bf = frag_rowk(sD, LDD, 16 * nt, ks);
-#pragma unroll
-        for (int mt = 0; mt < MTH; ++mt) acc_h[mt][nt] = Mma<T>::mma(af[mt], bf, acc_h[mt][nt]);
+        const frag bh = frag_rowk(sH, LDH, 16 * nt, ks * KW);
+        acc_d[nt] = Mma<T>::mma(o.wf[ks], bh, acc_d[nt]);
+        if constexpr (OUT) acc_o[nt] = Mma<T>::mma(o.qf[ks], bh, acc_o[nt]);
       }
+    // Delta = U - W h
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc_d[nt][i] = to_f32(o.u[nt][i]) - acc_d[nt][i];
+      store_acc_t(sD, LDD, rw, 16 * nt, acc_d[nt]);
     }
+    __syncthreads();  // Delta^T complete; all readers of h^T are done
+#pragma unroll
+    for (int mt = 0; mt < MTH; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc_h[mt][nt] *= o.eL;
+#pragma unroll
+    for (int ks = 0; ks < KS64; ++ks)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const frag bd = frag_rowk(sD, LDD, 16 * nt, ks * KW);
+        if constexpr (OUT) acc_o[nt] = Mma<T>::mma(o.pf[ks], bd, acc_o[nt]);
+#pragma unroll
+        for (int mt = 0; mt < MTH; ++mt) acc_h[mt][nt] = Mma<T>::mma(o.kf[mt][ks], bd, acc_h[mt][nt]);
+      }
 #pragma unroll
     for (int mt = 0; mt < MTH; ++mt)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) store_acc_t(sH, LDH, dkw + 16 * mt, 16 * nt, acc_h[mt][nt]);
+    if constexpr (OUT) {
+      // each wave stages its 16 output rows in LDS and writes them back as
+      // 16-byte pieces (LDS accesses of one wave are ordered: no barrier)
+      const int t0 = ts + c * CH;
+      const int len = min(CH, tl - c * CH);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) store_acc(sO, LDO, rw, 16 * nt, a.scale * acc_o[nt]);
+      constexpr int VE = 16 / sizeof(T);
+      constexpr int PPR = DVT / VE;  // 16-byte pieces per row
+      typedef float f4 __attribute__((ext_vector_type(4)));
+      T* op = (T*)a.o + ((int64_t)t0 * H + h) * DV + dv0;
+      // compile-time trip count: keeps the count of memory operations
+      // static, so the prefetched loads stay in flight across chunks
+#pragma unroll
+      for (int it = 0; it < (16 * PPR + 63) / 64; ++it) {
+        const int pc = l + 64 * it;
+        const int r = rw + pc / PPR, cc = (pc % PPR) * VE;
+        if (pc < 16 * PPR && r < len)
+          *reinterpret_cast<f4*>(op + (int64_t)r * H * DV + cc) = *reinterpret_cast<const f4*>(sO + r * LDO + cc);
+      }
+    }
+  };
+
+  // Chunk c lives in register stage c % S.  The main loop handles S chunks
+  // per trip with unconditional prefetches (the index is clamped to the last
+  // chunk, so the tail re-reads it): the number of memory operations between
+  // a prefetch and its use is then fixed, and the compiler's wait counts let
+  // the prefetched loads stay in flight.  A static tail runs the last
+  // nc % S chunks.
+  if (nc > 0) {
+    Ops st[S];
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s) load_ops(min(s, nc - 1), st[s]);
+    int cb = 0;
+    for (; cb + S <= nc; cb += S) {
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        load_ops(min(cb + s + S - 1, nc - 1), st[(s + S - 1) % S]);
+        process(cb + s, st[s]);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s)
+      if (cb + s < nc) process(cb + s, st[s]);
   }
   if (a.hT) {
 #pragma unroll
@@ -439,106 +537,15 @@ __global__ __launch_bounds__(256) void k_scan_fwd(const ScanFwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// k_out: per (chunk, head).  O = scale (diag(e^gamma) Q h + P Delta) with
-// P = Q K^T * Gam (diagonal included); DV in blocks of DVB.
-template <typename T, typename HS, int DK>
-__global__ __launch_bounds__(256) void k_out(const OutArgs a) {
-  constexpr int P = pad_of<T>();
-  constexpr int LDK = DK + P;
-  constexpr int L64 = 64 + P;
-  constexpr int DVB = dvb_of<T>();
-  constexpr int KW = Mma<T>::KW;
-  extern __shared__ __align__(16) char smem[];
-  T* sQ = (T*)smem;
-  T* sK = sQ + 64 * LDK;
-  T* sPT = sK + 64 * LDK;
-  T* sH = sPT + 64 * L64;
-  T* sD = sH + DVB * LDK;
-  float* sg = (float*)(sD + DVB * L64);
-
-  const int ci = blockIdx.x, h = blockIdx.y;
-  int n, t0, len;
-  if (!chunk_lookup(a.geo, ci, n, t0, len)) return;
-  const int H = a.geo.H, DV = a.DV;
-  const int tid = threadIdx.x, w = wave_id();
-  const int64_t ch = (int64_t)ci * H + h;
-  if (tid < 64) sg[tid] = a.gam[ch * 64 + tid];
-  load_rows<T, DK>(sQ, LDK, (const T*)a.q + ((int64_t)t0 * H + h) * DK, (int64_t)H * DK, len);
-  load_rows<T, DK>(sK, LDK, (const T*)a.k + ((int64_t)t0 * H + h) * DK, (int64_t)H * DK, len);
-  __syncthreads();
-  {
-    f32x4 acc[4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[nt] = zero4();
-#pragma unroll
-    for (int ks = 0; ks < DK; ks += KW) {
-      const auto af = frag_rowk(sQ, LDK, 16 * w, ks);
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[nt] = Mma<T>::mma(af, frag_rowk(sK, LDK, 16 * nt, ks), acc[nt]);
-    }
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + acc_row0() + i, s = 16 * nt + acc_col();
-        acc[nt][i] = (s <= r) ? acc[nt][i] * expf(sg[r] - sg[s]) : 0.f;
-      }
-      store_acc_t(sPT, L64, 16 * w, 16 * nt, acc[nt]);
-    }
-  }
-  float eg[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) eg[i] = expf(sg[16 * w + acc_row0() + i]);
-  T* op = (T*)a.o;
-  for (int dvb = 0; dvb < DV; dvb += DVB) {
-    __syncthreads();
-    load_rows_conv<HS, T, DK, DVB>(sH, LDK, (const HS*)a.hs + (ch * DV + dvb) * DK, DK, DVB);
-    load_rows<T, 64, DVB>(sD, L64, (const T*)a.Dt + (ch * DV + dvb) * 64, 64, DVB);
-    __syncthreads();
-    f32x4 acc[DVB / 16];
-#pragma unroll
-    for (int nt = 0; nt < DVB / 16; ++nt) acc[nt] = zero4();
-#pragma unroll
-    for (int ks = 0; ks < DK; ks += KW) {
-      const auto af = frag_rowk(sQ, LDK, 16 * w, ks);
-#pragma unroll
-      for (int nt = 0; nt < DVB / 16; ++nt) acc[nt] = Mma<T>::mma(af, frag_rowk(sH, LDK, 16 * nt, ks), acc[nt]);
-    }
-#pragma unroll
-    for (int nt = 0; nt < DVB / 16; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[nt][i] *= eg[i];
-#pragma unroll
-    for (int ks = 0; ks < 64; ks += KW) {
-      const auto af = frag_colk_lds(sPT, L64, 16 * w, ks);
-#pragma unroll
-      for (int nt = 0; nt < DVB / 16; ++nt) acc[nt] = Mma<T>::mma(af, frag_rowk(sD, L64, 16 * nt, ks), acc[nt]);
-    }
-#pragma unroll
-    for (int nt = 0; nt < DVB / 16; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + acc_row0() + i;
-        if (r < len) op[((int64_t)(t0 + r) * H + h) * DV + dvb + 16 * nt + acc_col()] = from_f32<T>(a.scale * acc[nt][i]);
-      }
-  }
-}
-
-// ---------------------------------------------------------------------------
 // host-side launchers
 
 template <typename T, int DK, bool BWD>
 static size_t wy_smem() {
   constexpr int P = pad_of<T>();
   constexpr int LDK = DK + P, L64 = 64 + P, LDF = 68, DVB = dvb_of<T>(), LDV = DVB + P;
-  constexpr int UNION = cmax(cmax(64 * LDF * 4, 64 * LDV * (int)sizeof(T)), BWD ? 64 * LDK * (int)sizeof(T) : 0);
-  return 64 * LDK * sizeof(T) + UNION + 64 * LDF * 4 + 2 * 64 * L64 * sizeof(T) + 4 * 16 * 20 * 4 + 4 * 64 * 4;
-}
-template <typename T, int DK>
-static size_t out_smem() {
-  constexpr int P = pad_of<T>();
-  constexpr int LDK = DK + P, L64 = 64 + P, DVB = dvb_of<T>();
-  return (2 * 64 * LDK + 64 * L64 + DVB * LDK + DVB * L64) * sizeof(T) + 64 * 4;
+  constexpr int R1 = cmax(cmax(2 * 64 * LDF * 4, (64 * LDK + 64 * LDV) * (int)sizeof(T)),
+                          (64 * LDK + 64 * L64) * (int)sizeof(T));
+  return 64 * LDK * sizeof(T) + R1 + 2 * 64 * L64 * sizeof(T) + 4 * 16 * 20 * 4 + 4 * 64 * 4;
 }
 
 template <typename T, int DK, bool BWD>
@@ -565,40 +572,29 @@ hipError_t launch_wy(const WyArgs& a, bool f32, int DK, bool bwd, hipStream_t st
   return bwd ? launch_wy_t<bf16, 128, true>(a, st) : launch_wy_t<bf16, 128, false>(a, st);
 }
 
-template <typename T, typename HS, int DK>
+template <typename T, typename HS, int DK, bool OUT>
 static hipError_t launch_scan_fwd_t(const ScanFwdArgs& a, int dvt, hipStream_t st) {
   const int Pn = a.geo.N * a.geo.H;
   const int grid = Pn * (a.DV / dvt);
   if (grid == 0) return hipSuccess;
-  if (dvt == 16) hipLaunchKernelGGL((k_scan_fwd<T, HS, DK, 16>), dim3(grid), dim3(256), 0, st, a);
-  else if (dvt == 32) hipLaunchKernelGGL((k_scan_fwd<T, HS, DK, 32>), dim3(grid), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((k_scan_fwd<T, HS, DK, 64>), dim3(grid), dim3(256), 0, st, a);
+  if (dvt == 16) hipLaunchKernelGGL((k_scan_fwd<T, HS, DK, 16, OUT>), dim3(grid), dim3(256), 0, st, a);
+  else if (dvt == 32) hipLaunchKernelGGL((k_scan_fwd<T, HS, DK, 32, OUT>), dim3(grid), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((k_scan_fwd<T, HS, DK, 64, OUT>), dim3(grid), dim3(256), 0, st, a);
   return hipGetLastError();
+}
+
+template <typename T, typename HS>
+static hipError_t launch_scan_fwd_d(const ScanFwdArgs& a, int DK, int dvt, hipStream_t st) {
+  const bool out = a.o != nullptr;
+  if (DK == 64) return out ? launch_scan_fwd_t<T, HS, 64, true>(a, dvt, st) : launch_scan_fwd_t<T, HS, 64, false>(a, dvt, st);
+  return out ? launch_scan_fwd_t<T, HS, 128, true>(a, dvt, st) : launch_scan_fwd_t<T, HS, 128, false>(a, dvt, st);
 }
 
 hipError_t launch_scan_fwd(const ScanFwdArgs& a, bool f32, int hs_dtype, int DK, int dvt, hipStream_t st) {
-  if (f32) return DK == 64 ? launch_scan_fwd_t<float, float, 64>(a, dvt, st) : launch_scan_fwd_t<float, float, 128>(a, dvt, st);
-  if (hs_dtype == GDR_F32)
-    return DK == 64 ? launch_scan_fwd_t<bf16, float, 64>(a, dvt, st) : launch_scan_fwd_t<bf16, float, 128>(a, dvt, st);
-  if (hs_dtype == GDR_F16)
-    return DK == 64 ? launch_scan_fwd_t<bf16, f16, 64>(a, dvt, st) : launch_scan_fwd_t<bf16, f16, 128>(a, dvt, st);
-  return DK == 64 ? launch_scan_fwd_t<bf16, bf16, 64>(a, dvt, st) : launch_scan_fwd_t<bf16, bf16, 128>(a, dvt, st);
-}
-
-template <typename T, typename HS, int DK>
-static hipError_t launch_out_t(const OutArgs& a, hipStream_t st) {
-  const size_t sm = out_smem<T, DK>();
-  hipError_t e = hipFuncSetAttribute((const void*)k_out<T, HS, DK>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_out<T, HS, DK>), dim3(a.geo.nchunks, a.geo.H), dim3(256), sm, st, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_out(const OutArgs& a, bool f32, int hs_dtype, int DK, hipStream_t st) {
-  if (f32) return DK == 64 ? launch_out_t<float, float, 64>(a, st) : launch_out_t<float, float, 128>(a, st);
-  if (hs_dtype == GDR_F32) return DK == 64 ? launch_out_t<bf16, float, 64>(a, st) : launch_out_t<bf16, float, 128>(a, st);
-  if (hs_dtype == GDR_F16) return DK == 64 ? launch_out_t<bf16, f16, 64>(a, st) : launch_out_t<bf16, f16, 128>(a, st);
-  return DK == 64 ? launch_out_t<bf16, bf16, 64>(a, st) : launch_out_t<bf16, bf16, 128>(a, st);
+  if (f32) return launch_scan_fwd_d<float, float>(a, DK, dvt, st);
+  if (hs_dtype == GDR_F32) return launch_scan_fwd_d<bf16, float>(a, DK, dvt, st);
+  if (hs_dtype == GDR_F16) return launch_scan_fwd_d<bf16, f16>(a, DK, dvt, st);
+  return launch_scan_fwd_d<bf16, bf16>(a, DK, dvt, st);
 }
 
 }  // namespace gdr

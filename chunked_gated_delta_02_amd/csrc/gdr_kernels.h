@@ -7,6 +7,10 @@
 
 #define GDR_MAX_SEQS 8192
 
+// per chunk-head gate block in the workspace: gamma[64], e^gamma[64],
+// e^{gamma_L - gamma}[64]
+#define GSTRIDE 192
+
 namespace gdr {
 
 // LDS row padding in elements: 16 bytes for 16-bit tiles (keeps 16-byte
@@ -17,6 +21,12 @@ template <typename T> constexpr int pad_of() { return sizeof(T) == 2 ? 8 : 4; }
 template <typename T> constexpr int dvb_of() { return sizeof(T) == 2 ? 64 : 32; }
 constexpr int cmax(int x, int y) { return x > y ? x : y; }
 
+// Workspace tensors are head-major, [H][slot][...], so the chunks of one
+// (sequence, head) are contiguous.  Operands the scans and the gradient
+// kernel feed to MFMA are stored in fragment order (afrag<R, K>: a wave's
+// fragment is one contiguous 1 KB block) and per-tile results in
+// accumulator order (acc<R, C>), so every access of the serial scans is a
+// fully coalesced wave-wide load or store.
 struct WyArgs {
   Geo geo;
   int DV;
@@ -24,42 +34,38 @@ struct WyArgs {
   const void* q;
   const void* k;
   const void* v;
+  const void* dO;    // backward only
   const float* beta;
   const float* g;
-  float* gam;   // [slot][H][64]
-  void* W;      // [slot][H][64][DK]
-  void* KtT;    // [slot][H][DK][64]
-  void* UT;     // [slot][H][DV][64]
-  float* Tm;    // [slot][H][64][64]       (backward)
-  void* WT;     // [slot][H][DK][64]       (backward)
-  void* PsT;    // [slot][H][64][64]       (backward)
-  void* QgsT;   // [slot][H][DK][64]       (backward)
+  float* gam;   // [GSTRIDE]: gamma, e^gamma, e^{gamma_L - gamma}
+  void* Wf;     // afrag<64, DK>: W (rows r, k = dk)
+  void* KtTf;   // afrag<DK, 64>: (E K)^T, E = e^{gamma_L - gamma} (nullable)
+  void* Ua;     // acc<64, DV>: U
+  void* Qgf;    // afrag<64, DK>: e^gamma Q                    (forward)
+  void* Pf;     // afrag<64, 64>: P = Q K^T * Gam (rows r)     (forward)
+  float* Tm;    // [64][64] fp32 row-major: T                 (backward)
+  void* WTf;    // afrag<DK, 64>: W^T                          (backward)
+  void* PsTf;   // afrag<64, 64>: scale P^T (rows s)           (backward)
+  void* QgsTf;  // afrag<DK, 64>: scale (e^gamma Q)^T          (backward)
+  void* Ktf;    // afrag<64, DK>: E K                          (backward)
+  void* dOf;    // afrag<DV, 64>: dO^T                         (backward)
 };
 
 struct ScanFwdArgs {
   Geo geo;
   int DV;
   int layout;        // 0: KV, 1: VK for h0 / hT
+  float scale;
   const float* h0;   // nullable
   float* hT;         // nullable
   const float* gam;
-  const void* W;
-  const void* KtT;
-  const void* UT;
-  void* hs;          // [slot][H][DV][DK] snapshots (state at chunk start), nullable
-  void* Dt;          // [slot][H][DV][64] Delta^T, nullable
-};
-
-struct OutArgs {
-  Geo geo;
-  int DV;
-  float scale;
-  const void* q;
-  const void* k;
-  const float* gam;
-  const void* hs;
-  const void* Dt;
+  const void* Wf;
+  const void* KtTf;
+  const void* Ua;
+  const void* Qgf;   // output operands (o == nullptr: no output)
+  const void* Pf;
   void* o;
+  void* hs;          // acc<DK, DV> per chunk-head: state at chunk start (required)
 };
 
 struct ScanBwdArgs {
@@ -68,14 +74,14 @@ struct ScanBwdArgs {
   int layout;
   const float* dhT;  // nullable
   float* dh0;        // nullable
-  const void* k;
-  const void* dO;
   const float* gam;
-  const void* PsT;
-  const void* QgsT;
-  const void* WT;
-  void* dhs;         // [slot][H][DK][DV] gradient of the state at chunk end
-  void* dD;          // [slot][H][64][DV] gradient of Delta
+  const void* Ktf;
+  const void* PsTf;
+  const void* QgsTf;
+  const void* WTf;
+  const void* dOf;
+  void* dhs;         // acc<DK, DV>: gradient of the state at chunk end
+  void* dD;          // acc<64, DV>: gradient of Delta
 };
 
 struct GradArgs {
@@ -88,8 +94,8 @@ struct GradArgs {
   const void* dO;
   const float* beta;
   const float* gam;
-  const void* W;
-  const void* UT;
+  const void* Wf;
+  const void* Ua;
   const float* Tm;
   const void* hs;
   const void* dhs;
@@ -154,6 +160,36 @@ __device__ __forceinline__ void store8(T* dst, const float* v) {
   }
 }
 
+// Write rows [0, RB) of an afrag<*, K> matrix (dst already points at the
+// first fragment of row tile i0 / 16) with element (i, k) = f(i, k).  Each
+// thread writes 16-byte pieces; consecutive threads write consecutive pieces.
+template <typename T, int RB, int K, typename F>
+__device__ __forceinline__ void write_afrag(T* dst, F&& f) {
+  constexpr int KW = Mma<T>::KW, KPL = Mma<T>::KPL;
+  constexpr int PE = 16 / sizeof(T);                // elements per piece
+  constexpr int NPIECE = RB * K / PE;
+  for (int p = threadIdx.x; p < NPIECE; p += blockDim.x) {
+    float v[PE];
+#pragma unroll
+    for (int j = 0; j < PE; ++j) {
+      const int off = p * PE + j;
+      const int fr = off / (64 * KPL), rem = off - fr * (64 * KPL);
+      const int l = rem / KPL, jj = rem - l * KPL;
+      const int m = fr / (K / KW), s = fr - m * (K / KW);
+      v[j] = f(16 * m + (l & 15), KW * s + KPL * (l >> 4) + jj);
+    }
+    if constexpr (PE == 8) {
+      typedef T t8 __attribute__((ext_vector_type(8)));
+      t8 w;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) w[j] = from_f32<T>(v[j]);
+      *reinterpret_cast<t8*>(dst + (int64_t)p * PE) = w;
+    } else {
+      *reinterpret_cast<f32x4*>(dst + (int64_t)p * PE) = (f32x4){v[0], v[1], v[2], v[3]};
+    }
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ f32x4 load4f(const T* p) {
   if constexpr (sizeof(T) == 2) {
@@ -170,7 +206,6 @@ hipError_t launch_plan(const int* cu, int N, int T_total, int nchunks, int* seq_
                        hipStream_t st);
 hipError_t launch_wy(const WyArgs& a, bool f32, int DK, bool bwd, hipStream_t st);
 hipError_t launch_scan_fwd(const ScanFwdArgs& a, bool f32, int hs_dtype, int DK, int dvt, hipStream_t st);
-hipError_t launch_out(const OutArgs& a, bool f32, int hs_dtype, int DK, hipStream_t st);
 hipError_t launch_scan_bwd(const ScanBwdArgs& a, bool f32, int DK, int dvt, hipStream_t st);
 hipError_t launch_grad(const GradArgs& a, bool f32, int hs_dtype, int DK, hipStream_t st);
 

@@ -32,8 +32,9 @@
  *
  * Ownership and errors.  The caller owns and allocates every buffer,
  * including the workspace; the library never allocates, keeps no state
- * between calls and is safe to call concurrently from several host threads
- * on different streams (each call needs its own workspace).  Every argument
+ * between calls (apart from the opt-in per-thread diagnostic timers below)
+ * and is safe to call concurrently from several host threads on different
+ * streams (each call needs its own workspace).  Every argument
  * error is detected on the host before any launch: the call returns a status,
  * launches nothing and writes nothing.  gdr_last_error() returns a message
  * for the calling thread's last failed call.  Work is enqueued on the given
@@ -90,9 +91,10 @@ size_t gdr_fwd_workspace_bytes(const gdr_problem* p);
 size_t gdr_bwd_workspace_bytes(const gdr_problem* p, int have_h_saved);
 
 /* Size of the per-chunk state snapshots that gdr_chunk_fwd can save for
- * gdr_chunk_bwd: one DV x DK state (VK order) per chunk slot and head, in
- * h_store_dtype.  Chunk slots: B * ceil(T/64) for fixed-length batches,
- * ceil(T/64) + N for packed ones. */
+ * gdr_chunk_bwd: one DV x DK state per chunk slot and head, in
+ * h_store_dtype (an opaque buffer: only gdr_chunk_bwd reads it).  Chunk
+ * slots: B * ceil(T/64) for fixed-length batches, ceil(T/64) + N for packed
+ * ones. */
 size_t gdr_h_saved_bytes(const gdr_problem* p);
 
 /* Forward.  Writes o; writes hT if non-NULL; writes the state snapshots to
@@ -115,13 +117,12 @@ gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, con
 /* Diagnostics: per-kernel timing with caller-owned HIP events.
  * Kernel ids of the launches a forward / backward call makes: */
 enum {
-  GDR_KERNEL_PLAN = 0,       /* packed batches: cu_seqlens -> chunk table       */
-  GDR_KERNEL_WY = 1,         /* gamma, T = (I + A)^-1, W, U (and bwd extras)    */
-  GDR_KERNEL_SCAN_FWD = 2,   /* inter-chunk state scan (also the bwd recompute) */
-  GDR_KERNEL_OUT = 3,        /* forward output                                  */
-  GDR_KERNEL_SCAN_BWD = 4,   /* reverse dh scan                                 */
-  GDR_KERNEL_GRAD = 5,       /* fused chunk-parallel gradient kernel            */
-  GDR_NUM_KERNELS = 6
+  GDR_KERNEL_PLAN = 0,       /* packed batches: cu_seqlens -> chunk table          */
+  GDR_KERNEL_WY = 1,         /* gamma, T = (I + A)^-1, W, U, P (and bwd extras)    */
+  GDR_KERNEL_SCAN_FWD = 2,   /* state scan with fused output (bwd: recompute only) */
+  GDR_KERNEL_SCAN_BWD = 3,   /* reverse dh scan                                    */
+  GDR_KERNEL_GRAD = 4,       /* fused chunk-parallel gradient kernel               */
+  GDR_NUM_KERNELS = 5
 };
 /* events: NULL to switch timing off for the calling thread, else an array of
  * 2 * GDR_NUM_KERNELS hipEvent_t handles (start, stop per kernel id; NULL
