@@ -7,8 +7,10 @@ gdr_chunk_bwd on one batch of the fixed-length bf16 workload B=2, T=4096,
 H=16, DK=DV=128 (seeded synthetic inputs, resident in HBM before the timed
 region).  Prints ONE JSON line.  Per-kernel durations come from HIP events
 that libgdr records around each launch on the call's stream (opt-in
-diagnostic timers); the dominant kernel's roofline uses the algorithmic
-byte / flop model of each kernel stated below.
+diagnostic timers).  The dominant kernel's roofline uses its algorithmic
+bytes (operator inputs read and outputs written once) and GEMM flops; the
+per-kernel "kernels" entries use an implementation byte model (every tensor
+and workspace buffer the kernel touches, once).
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -61,32 +63,41 @@ def flops_bwd(K, V, C=CH):
 # token-heads.  e = io element size, hs = snapshot element size.
 
 def kernel_model(name, mode, NC, NP, NT, K, V, e, hs, C=CH):
+    G = C * 4 * 3  # gate block per chunk-head: gamma, e^gamma, e^{gamma_L - gamma}
     if name == "wy":
-        # reads q, k, v, beta, g; writes gamma, W, Kt^T, U^T and P (fwd) or
-        # T, W^T, scale P^T, scale Qg^T (bwd)
-        rd = NT * (2 * K * e + V * e + 8)
-        wr = NC * (C * 4 + C * K * e + K * C * e + V * C * e + C * C * e)
+        # reads q, k, v, beta, g (+ dO); writes the gate block, W, U and
+        # (fwd) Kt^T, e^gamma Q, P or (bwd) T, W^T, E K, dO^T, scale P^T,
+        # scale (e^gamma Q)^T
         fl = NC * (2 * C * C * K + C ** 3 / 3.0 + 2 * C * C * K + 2 * C * C * V + 2 * C * C * K)
-        if mode == "bwd":
-            wr += NC * (C * C * 4 + K * C * e + K * C * e)
+        if mode == "fwd":
+            rd = NT * (2 * K * e + V * e + 8)
+            wr = NC * (G + C * K * e + C * V * e + K * C * e + C * K * e + C * C * e)
+        else:
+            rd = NT * (2 * K * e + 2 * V * e + 8)
+            wr = NC * (G + C * K * e + C * V * e + C * C * 4 + K * C * e + C * K * e + V * C * e
+                       + C * C * e + K * C * e)
         return rd + wr, fl
     if name == "scan_fwd":
-        # reads W, Kt^T, U^T, gamma (+ q, P with the fused output); writes the
+        # reads W, Kt^T, U (+ e^gamma Q, P with the fused output); writes the
         # snapshots (+ o); h0 / hT per (sequence, head)
-        rd = NC * (2 * C * K * e + V * C * e + C * 4) + NP * K * V * 4
+        rd = NC * (2 * C * K * e + C * V * e + 4) + NP * K * V * 4
         wr = NC * K * V * hs + NP * K * V * 4
         fl = NC * 4 * C * K * V
         if mode == "fwd":
-            rd += NT * K * e + NC * C * C * e
+            rd += NC * (C * K * e + C * C * e)
             wr += NT * V * e
             fl += NC * (2 * C * K * V + 2 * C * C * V)
         return rd + wr, fl
     if name == "scan_bwd":
-        rd = NT * (K * e + V * e) + NC * (C * C * e + 2 * K * C * e + 4) + NP * K * V * 4
+        # reads E K, scale P^T, scale (e^gamma Q)^T, W^T, dO^T; writes the dh
+        # snapshots and dDelta; dhT / dh0 per (sequence, head)
+        rd = NC * (C * K * e + C * C * e + 2 * K * C * e + V * C * e + 4) + NP * K * V * 4
         wr = NC * (K * V * e + C * V * e) + NP * K * V * 4
         return rd + wr, NC * (6 * C * K * V + 2 * C * C * V)
     if name == "grad":
-        rd = NT * (2 * K * e + 2 * V * e + 4) + NC * (C * 4 + C * K * e + V * C * e + C * C * 4
+        # reads q, k, v, dO, beta, the gate block, T, W, U, the h and dh
+        # snapshots and dDelta; writes dq, dk, dv, dbeta, dg
+        rd = NT * (2 * K * e + 2 * V * e + 4) + NC * (G + C * C * 4 + C * K * e + C * V * e
                                                       + K * V * hs + K * V * e + C * V * e)
         wr = NT * (2 * K * e + V * e + 8)
         fl = NC * (8 * C * K * V + 6 * C * C * V + 14 * C * C * K + 4 * C ** 3)
@@ -94,6 +105,26 @@ def kernel_model(name, mode, NC, NP, NT, K, V, e, hs, C=CH):
     if name == "plan":
         return 0, 0
     raise KeyError(name)
+
+
+# Algorithmic bytes of a kernel: the operator's own inputs it must read and
+# outputs it must write, each once (workspace and snapshots are implementation
+# choices and are not counted).  k_grad reads every per-token input of the
+# backward and writes every per-token gradient: per token-head
+# (2 K e + 2 V e + 8) + (2 K e + V e + 8) bytes.  `states` = number of
+# per-(sequence, head) fp32 state tensors the kernel reads or writes.
+
+def algorithmic_bytes(name, mode, NT, NP, K, V, e, states):
+    st = states * NP * K * V * 4
+    if name == "grad":
+        return NT * ((2 * K * e + 2 * V * e + 8) + (2 * K * e + V * e + 8))
+    if name == "wy":
+        return NT * (2 * K * e + V * e + 8 + (V * e if mode == "bwd" else 0))
+    if name == "scan_fwd":
+        return (NT * V * e if mode == "fwd" else 0) + st
+    if name == "scan_bwd":
+        return st
+    return 0
 
 
 # ---------------------------------------------------------------------------
@@ -285,7 +316,11 @@ def main():
 
     tokens = B * T
     NT = B * T * H
-    NC = B * ((T + CH - 1) // CH) * H if cu is None else None
+    if cu is None:
+        NC = B * ((T + CH - 1) // CH) * H
+    else:
+        lens = (inp["cu_seqlens"][1:] - inp["cu_seqlens"][:-1]).tolist()
+        NC = sum((n + CH - 1) // CH for n in lens) * H
     NP = N * H
     e = q.element_size()
     hs = hs_dt.itemsize
@@ -301,7 +336,9 @@ def main():
                         "TFLOPs": round(fl / (ms * 1e-3) / 1e12, 2)}
     dom = max(per, key=per.get)
     phase, kname = dom.split(".")
-    byt, fl = kernel_model(kname, phase, NC, NP, NT, K, V, e, hs)
+    _, fl = kernel_model(kname, phase, NC, NP, NT, K, V, e, hs)
+    nstates = {("scan_fwd", "fwd"): (h0 is not None) + 1, ("scan_bwd", "bwd"): (dhT is not None) + 1}
+    byt = algorithmic_bytes(kname, phase, NT, NP, K, V, e, nstates.get((kname, phase), 0))
     t_dom = per[dom] * 1e-3
     if byt / PEAK_HBM >= fl / peak:
         roof = {"bound": "hbm", "achieved": round(byt / t_dom / 1e9, 1), "peak": PEAK_HBM / 1e9,

@@ -218,7 +218,7 @@ __global__ __launch_bounds__(256) void k_scan_bwd(const ScanBwdArgs a) {
 // stay inside one wavefront; column sums go through per-wave LDS partials
 // reduced in a fixed order.
 template <typename T, typename HS, int DK>
-__global__ __launch_bounds__(256) void k_grad(const GradArgs a) {
+__global__ __launch_bounds__(256, 2) void k_grad(const GradArgs a) {
   constexpr int P = pad_of<T>();
   constexpr int LDK = DK + P;
   constexpr int L64 = 64 + P;
