@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--h-store", choices=("f32", "f16", "bf16"), default=None,
+                    help="snapshot dtype (default: the workload's)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the oracle sample")
     return ap.parse_args()
@@ -62,43 +64,56 @@ def flops_bwd(K, V, C=CH):
 # performs (2mnk), for NC chunk-heads, NP (sequence, head) pairs and NT
 # token-heads.  e = io element size, hs = snapshot element size.
 
-def kernel_model(name, mode, NC, NP, NT, K, V, e, hs, C=CH):
+def kernel_model(name, mode, NC, NP, NT, K, V, e, hs, cp=1, C=CH):
     G = C * 4 * 3  # gate block per chunk-head: gamma, e^gamma, e^{gamma_L - gamma}
+    if name in ("cp_scan_fwd", "cp_scan_bwd"):
+        # segment summaries: the scan over all but one segment of every
+        # sequence with DK + DV columns, no per-chunk outputs; writes the
+        # DK x (DK + DV) summary per (segment, sequence, head)
+        f = (cp - 1) / cp
+        if name == "cp_scan_fwd":
+            rd = f * NC * (2 * C * K * e + C * V * 4 + 4)
+        else:
+            rd = f * NC * (2 * C * K * e + C * V * 4 + K * V * 4 + 4)
+        fl = f * NC * 4 * C * K * (K + V)
+        return rd + (cp - 1) * NP * K * (K + V) * 4, fl
+    if name in ("cp_chain_fwd", "cp_chain_bwd"):
+        return (cp - 1) * NP * (K * (K + V) + K * V) * 4, (cp - 1) * NP * 2 * K * K * V
     if name == "wy":
-        # reads q, k, v, beta, g (+ dO); writes the gate block, W, U and
-        # (fwd) Kt^T, e^gamma Q, P or (bwd) T, W^T, E K, dO^T, scale P^T,
-        # scale (e^gamma Q)^T
+        # reads q, k, v, beta, g (+ dO); writes the gate block, W, U (fp32)
+        # and (fwd) K^T, Q, P (split: hi + lo) or (bwd) T, W^T, K,
+        # scale P^T dO and scale (e^gamma Q)^T dO (fp32)
         fl = NC * (2 * C * C * K + C ** 3 / 3.0 + 2 * C * C * K + 2 * C * C * V + 2 * C * C * K)
         if mode == "fwd":
             rd = NT * (2 * K * e + V * e + 8)
-            wr = NC * (G + C * K * e + C * V * e + K * C * e + C * K * e + C * C * e)
+            wr = NC * (G + C * K * e + C * V * 4 + K * C * e + C * K * e + C * C * e * (1 if e == 4 else 2))
         else:
             rd = NT * (2 * K * e + 2 * V * e + 8)
-            wr = NC * (G + C * K * e + C * V * e + C * C * 4 + K * C * e + C * K * e + V * C * e
-                       + C * C * e + K * C * e)
+            wr = NC * (G + C * K * e + C * V * 4 + C * C * 4 + K * C * e + C * K * e + C * V * 4 + K * V * 4)
+            fl += NC * (2 * C * C * V + 2 * C * K * V)
         return rd + wr, fl
     if name == "scan_fwd":
-        # reads W, Kt^T, U (+ e^gamma Q, P with the fused output); writes the
-        # snapshots (+ o); h0 / hT per (sequence, head)
-        rd = NC * (2 * C * K * e + C * V * e + 4) + NP * K * V * 4
+        # reads W, K^T, U (+ Q, P with the output); writes the snapshots
+        # (+ o); h0 / hT per (sequence, head)
+        rd = NC * (2 * C * K * e + C * V * 4 + 4) + NP * K * V * 4
         wr = NC * K * V * hs + NP * K * V * 4
         fl = NC * 4 * C * K * V
         if mode == "fwd":
-            rd += NC * (C * K * e + C * C * e)
+            rd += NC * (C * K * e + C * C * e * (1 if e == 4 else 2))
             wr += NT * V * e
             fl += NC * (2 * C * K * V + 2 * C * C * V)
         return rd + wr, fl
     if name == "scan_bwd":
-        # reads E K, scale P^T, scale (e^gamma Q)^T, W^T, dO^T; writes the dh
-        # snapshots and dDelta; dhT / dh0 per (sequence, head)
-        rd = NC * (C * K * e + C * C * e + 2 * K * C * e + V * C * e + 4) + NP * K * V * 4
-        wr = NC * (K * V * e + C * V * e) + NP * K * V * 4
-        return rd + wr, NC * (6 * C * K * V + 2 * C * C * V)
+        # reads K, W^T, scale P^T dO and scale Qg^T dO (fp32); writes the dh
+        # snapshots and dDelta (fp32); dhT / dh0 per (sequence, head)
+        rd = NC * (2 * C * K * e + C * V * 4 + K * V * 4 + 4) + NP * K * V * 4
+        wr = NC * (K * V * e + C * V * 4) + NP * K * V * 4
+        return rd + wr, NC * 4 * C * K * V
     if name == "grad":
         # reads q, k, v, dO, beta, the gate block, T, W, U, the h and dh
         # snapshots and dDelta; writes dq, dk, dv, dbeta, dg
-        rd = NT * (2 * K * e + 2 * V * e + 4) + NC * (G + C * C * 4 + C * K * e + C * V * e
-                                                      + K * V * hs + K * V * e + C * V * e)
+        rd = NT * (2 * K * e + 2 * V * e + 4) + NC * (G + C * C * 4 + C * K * e + C * V * 4
+                                                      + K * V * hs + K * V * e + C * V * 4)
         wr = NT * (2 * K * e + V * e + 8)
         fl = NC * (8 * C * K * V + 6 * C * C * V + 14 * C * C * K + 4 * C ** 3)
         return rd + wr, fl
@@ -233,8 +248,8 @@ def main():
     from chunked_gated_delta_02_amd import _lib, inputs as gin, ops
 
     w = gin.CONFIGS[args.config]
-    if w.cp_segments != 1:
-        w = w.replace(cp_segments=1)
+    if args.h_store:
+        w = w.replace(h_store=args.h_store)
     inp = gin.generate(w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -244,7 +259,7 @@ def main():
     B, T, H, K = q.shape
     V = v.shape[-1]
     N = inp["N"]
-    p = ops.make_problem(q, v, cu, w.layout, None, w.h_store)
+    p = ops.make_problem(q, v, cu, w.layout, None, w.h_store, w.cp_segments)
     st = _lib.gdr_check(p)
     if st != _lib.GDR_OK:
         raise _lib.GDRError(st, _lib.last_error())
@@ -331,12 +346,12 @@ def main():
     kernels = {}
     for key, ms in per.items():
         phase, kname = key.split(".")
-        byt, fl = kernel_model(kname, phase, NC, NP, NT, K, V, e, hs)
+        byt, fl = kernel_model(kname, phase, NC, NP, NT, K, V, e, hs, w.cp_segments)
         kernels[key] = {"avg_us": round(ms * 1e3, 2), "GBps": round(byt / (ms * 1e-3) / 1e9, 1),
                         "TFLOPs": round(fl / (ms * 1e-3) / 1e12, 2)}
     dom = max(per, key=per.get)
     phase, kname = dom.split(".")
-    _, fl = kernel_model(kname, phase, NC, NP, NT, K, V, e, hs)
+    _, fl = kernel_model(kname, phase, NC, NP, NT, K, V, e, hs, w.cp_segments)
     nstates = {("scan_fwd", "fwd"): (h0 is not None) + 1, ("scan_bwd", "bwd"): (dhT is not None) + 1}
     byt = algorithmic_bytes(kname, phase, NT, NP, K, V, e, nstates.get((kname, phase), 0))
     t_dom = per[dom] * 1e-3
@@ -368,7 +383,7 @@ def main():
         "dtype": "bf16" if q.dtype == torch.bfloat16 else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "T": T, "H": H, "DK": K, "DV": V, "chunk": CH,
-                   "layout": w.layout, "h_store": w.h_store, "seed": w.seed,
+                   "layout": w.layout, "h_store": w.h_store, "cp_segments": w.cp_segments, "seed": w.seed,
                    "parallelism": "single GPU"},
         "tflops": {"fwd+bwd": round((fl_f + fl_b) / (ms_step * 1e-3) / 1e12, 2),
                    "fwd_kernels": round(fl_f / (fwd_ms * 1e-3) / 1e12, 2) if fwd_ms else None,

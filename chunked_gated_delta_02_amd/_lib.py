@@ -21,7 +21,8 @@ GDR_LAYOUT_KV, GDR_LAYOUT_VK = 0, 1
 EXPORTS = ("gdr_check", "gdr_fwd_workspace_bytes", "gdr_bwd_workspace_bytes", "gdr_h_saved_bytes",
            "gdr_chunk_fwd", "gdr_chunk_bwd", "gdr_set_kernel_timers", "gdr_status_string",
            "gdr_last_error", "gdr_version")
-KERNELS = ("plan", "wy", "scan_fwd", "scan_bwd", "grad")
+KERNELS = ("plan", "wy", "scan_fwd", "scan_bwd", "grad", "cp_scan_fwd", "cp_chain_fwd", "cp_scan_bwd",
+           "cp_chain_bwd")
 
 
 class gdr_problem(ctypes.Structure):

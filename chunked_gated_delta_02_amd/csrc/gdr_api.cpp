@@ -58,7 +58,7 @@ gdr_status check_problem(const gdr_problem* p) {
   }
   if (p->layout != GDR_LAYOUT_KV && p->layout != GDR_LAYOUT_VK) { set_err("layout must be GDR_LAYOUT_KV or GDR_LAYOUT_VK"); return GDR_ERR_INVALID_ARG; }
   if (p->cp_segments < 1) { set_err("cp_segments must be >= 1 (got %d)", p->cp_segments); return GDR_ERR_INVALID_ARG; }
-  if (p->cp_segments != 1) { set_err("intra-card context parallelism (cp_segments > 1) is not available in this build"); return GDR_ERR_UNSUPPORTED; }
+  if (p->cp_segments > 1024) { set_err("cp_segments must be <= 1024 (got %d)", p->cp_segments); return GDR_ERR_UNSUPPORTED; }
   const double tokens = (double)p->batch * p->seqlen;
   if (tokens * p->heads * (p->dv > p->dk ? p->dv : p->dk) > 4.0e12) { set_err("problem too large"); return GDR_ERR_UNSUPPORTED; }
   return GDR_OK;
@@ -68,8 +68,9 @@ struct Plan {
   int N = 0, NCb = 0, ncps = 0;
   bool f32 = false;
   size_t esz = 2, hsz = 4;
-  size_t seq_chunk = 0, chunk_seq = 0, gam = 0, Wf = 0, KtTf = 0, Ua = 0, hs = 0, Qgf = 0, Pf = 0;
-  size_t Tm = 0, WTf = 0, PsTf = 0, QgsTf = 0, Ktf = 0, dOf = 0, dhs = 0, dD = 0;
+  size_t seq_chunk = 0, chunk_seq = 0, gam = 0, Wf = 0, KtTf = 0, Ua = 0, hs = 0, Qf = 0, Pf = 0, Pfl = 0;
+  size_t Tm = 0, WTf = 0, Kf = 0, dDl = 0, Z = 0, dhs = 0, dD = 0;
+  size_t summ = 0, hst = 0;   // CP segment summaries and hand-off states
   size_t total = 0;
 };
 
@@ -98,24 +99,29 @@ Plan make_plan(const gdr_problem* p, int mode, bool need_hs) {
   }
   pl.gam = take(ch * GSTRIDE * 4);
   pl.Wf = take(ch * 64 * DK * e);
-  pl.Ua = take(ch * 64 * DV * e);
+  pl.Ua = take(ch * 64 * DV * 4);
   if (need_hs) {
     pl.hs = take(ch * DV * DK * pl.hsz);
     pl.KtTf = take(ch * DK * 64 * e);
   }
   if (mode == 0) {
     if (!need_hs) pl.KtTf = take(ch * DK * 64 * e);
-    pl.Qgf = take(ch * 64 * DK * e);
+    pl.Qf = take(ch * 64 * DK * e);
     pl.Pf = take(ch * 64 * 64 * e);
+    if (!pl.f32) pl.Pfl = take(ch * 64 * 64 * e);
   } else {
     pl.Tm = take(ch * 64 * 64 * 4);
     pl.WTf = take(ch * DK * 64 * e);
-    pl.PsTf = take(ch * 64 * 64 * e);
-    pl.QgsTf = take(ch * DK * 64 * e);
-    pl.Ktf = take(ch * 64 * DK * e);
-    pl.dOf = take(ch * DV * 64 * e);
+    pl.Kf = take(ch * 64 * DK * e);
+    pl.dDl = take(ch * 64 * DV * 4);
+    pl.Z = take(ch * DK * DV * 4);
     pl.dhs = take(ch * DK * DV * e);
-    pl.dD = take(ch * 64 * DV * e);
+    pl.dD = take(ch * 64 * DV * 4);
+  }
+  if (p->cp_segments > 1) {
+    const size_t units = (size_t)p->cp_segments * pl.N * p->heads;
+    pl.summ = take(units * DK * (DK + DV) * 4);
+    pl.hst = take(units * DK * DV * 4);
   }
   pl.total = o + 256;  // slack for base alignment
   return pl;
@@ -134,16 +140,19 @@ gdr::Geo make_geo(const gdr_problem* p, const Plan& pl, const int32_t* cu, char*
   g.cu = p->varlen ? cu : nullptr;
   g.seq_chunk = p->varlen ? (const int*)(ws + pl.seq_chunk) : nullptr;
   g.chunk_seq = p->varlen ? (const int*)(ws + pl.chunk_seq) : nullptr;
+  g.cp = p->cp_segments;
   return g;
 }
 
-// DV tile of the serial scans: the largest of 64 / 32 / 16 that still gives
-// at least two workgroups per compute unit (512), else 16.  The fp32 path
-// always uses 16 (its operand fragments are 8x larger per k).
-int pick_dvt(int units, int dv, bool f32) {
+// Column tile of the serial scans.  A wider tile reads each chunk operand
+// once for more columns, a narrower one gives more workgroups: take the
+// widest that still gives two workgroups per compute unit (512 in all), among
+// the tiles that fit in registers without spilling (64 only with DK = 64).
+// The fp32 path always uses 16 (its operand fragments are 8x larger per k).
+int pick_dvt(long units, int cols, bool f32, int dk) {
   if (f32) return 16;
-  if ((long)units * (dv / 64) >= 512) return 64;
-  if ((long)units * (dv / 32) >= 512) return 32;
+  if (dk == 64 && units * (cols / 64) >= 512) return 64;
+  if (units * (cols / 32) >= 512) return 32;
   return 16;
 }
 
@@ -223,15 +232,22 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, con
     gdr::WyArgs wa{};
     wa.geo = geo; wa.DV = p->dv; wa.scale = scale;
     wa.q = q; wa.k = k; wa.v = v; wa.beta = beta; wa.g = g;
-    wa.gam = (float*)(ws + pl.gam); wa.Wf = ws + pl.Wf; wa.KtTf = ws + pl.KtTf; wa.Ua = ws + pl.Ua;
-    wa.Qgf = ws + pl.Qgf; wa.Pf = ws + pl.Pf;
+    wa.gam = (float*)(ws + pl.gam); wa.Wf = ws + pl.Wf; wa.KtTf = ws + pl.KtTf; wa.Ua = (float*)(ws + pl.Ua);
+    wa.Qf = ws + pl.Qf; wa.Pf = ws + pl.Pf; wa.Pfl = pl.f32 ? nullptr : (void*)(ws + pl.Pfl);
     GDR_LAUNCH(GDR_KERNEL_WY, s, gdr::launch_wy(wa, pl.f32, p->dk, false, s));
   }
   gdr::ScanFwdArgs sa{};
   sa.geo = geo; sa.DV = p->dv; sa.layout = p->layout; sa.scale = scale; sa.h0 = h0; sa.hT = hT;
-  sa.gam = (const float*)(ws + pl.gam); sa.Wf = ws + pl.Wf; sa.KtTf = ws + pl.KtTf; sa.Ua = ws + pl.Ua;
-  sa.Qgf = ws + pl.Qgf; sa.Pf = ws + pl.Pf; sa.o = o; sa.hs = hs;
-  GDR_LAUNCH(GDR_KERNEL_SCAN_FWD, s, gdr::launch_scan_fwd(sa, pl.f32, p->h_store_dtype, p->dk, pick_dvt(pl.N * p->heads, p->dv, pl.f32), s));
+  sa.gam = (const float*)(ws + pl.gam); sa.Wf = ws + pl.Wf; sa.KtTf = ws + pl.KtTf; sa.Ua = (const float*)(ws + pl.Ua);
+  sa.Qf = ws + pl.Qf; sa.Pf = ws + pl.Pf; sa.Pfl = ws + pl.Pfl; sa.o = o; sa.hs = hs;
+  const long units = (long)pl.N * p->cp_segments * p->heads;
+  if (p->cp_segments > 1) {
+    sa.summ = (float*)(ws + pl.summ); sa.hstart = (const float*)(ws + pl.hst);
+    GDR_LAUNCH(GDR_KERNEL_CP_SCAN_FWD, s, gdr::launch_scan_fwd(sa, pl.f32, p->h_store_dtype, p->dk, pick_dvt(units, p->dk + p->dv, pl.f32, p->dk), 0, s));
+    gdr::CpChainArgs ca{geo, p->dk, p->dv, p->layout, 0, h0, (const float*)(ws + pl.summ), (float*)(ws + pl.hst)};
+    GDR_LAUNCH(GDR_KERNEL_CP_CHAIN_FWD, s, gdr::launch_cp_chain(ca, s));
+  }
+  GDR_LAUNCH(GDR_KERNEL_SCAN_FWD, s, gdr::launch_scan_fwd(sa, pl.f32, p->h_store_dtype, p->dk, pick_dvt(units, p->dv, pl.f32, p->dk), 2, s));
   return GDR_OK;
 }
 
@@ -262,7 +278,9 @@ gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, con
   const float scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->dk);
   gdr::Geo geo = make_geo(p, pl, cu_seqlens, ws);
   const void* hs = h_saved ? h_saved : (const void*)(ws + pl.hs);
-  const int dvt = pick_dvt(pl.N * p->heads, p->dv, pl.f32);
+  const long units = (long)pl.N * p->cp_segments * p->heads;
+  const int dvt = pick_dvt(units, p->dv, pl.f32, p->dk);
+  const int dvt_cp = pick_dvt(units, p->dk + p->dv, pl.f32, p->dk);
 
   if (p->varlen)
     GDR_LAUNCH(GDR_KERNEL_PLAN, s, gdr::launch_plan(cu_seqlens, pl.N, p->seqlen, pl.NCb, (int*)(ws + pl.seq_chunk), (int*)(ws + pl.chunk_seq), s));
@@ -270,30 +288,43 @@ gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, con
     gdr::WyArgs wa{};
     wa.geo = geo; wa.DV = p->dv; wa.scale = scale;
     wa.q = q; wa.k = k; wa.v = v; wa.dO = dO; wa.beta = beta; wa.g = g;
-    wa.gam = (float*)(ws + pl.gam); wa.Wf = ws + pl.Wf; wa.Ua = ws + pl.Ua;
+    wa.gam = (float*)(ws + pl.gam); wa.Wf = ws + pl.Wf; wa.Ua = (float*)(ws + pl.Ua);
     wa.KtTf = h_saved ? nullptr : (void*)(ws + pl.KtTf);
-    wa.Tm = (float*)(ws + pl.Tm); wa.WTf = ws + pl.WTf; wa.PsTf = ws + pl.PsTf; wa.QgsTf = ws + pl.QgsTf;
-    wa.Ktf = ws + pl.Ktf; wa.dOf = ws + pl.dOf;
+    wa.Tm = (float*)(ws + pl.Tm); wa.WTf = ws + pl.WTf; wa.Kf = ws + pl.Kf;
+    wa.dDl = (float*)(ws + pl.dDl); wa.Z = (float*)(ws + pl.Z);
     GDR_LAUNCH(GDR_KERNEL_WY, s, gdr::launch_wy(wa, pl.f32, p->dk, true, s));
     if (!h_saved) {
       gdr::ScanFwdArgs sa{};
       sa.geo = geo; sa.DV = p->dv; sa.layout = p->layout; sa.scale = scale; sa.h0 = h0; sa.hT = nullptr;
-      sa.gam = (const float*)(ws + pl.gam); sa.Wf = ws + pl.Wf; sa.KtTf = ws + pl.KtTf; sa.Ua = ws + pl.Ua;
-      sa.Qgf = nullptr; sa.Pf = nullptr; sa.o = nullptr; sa.hs = ws + pl.hs;
-      GDR_LAUNCH(GDR_KERNEL_SCAN_FWD, s, gdr::launch_scan_fwd(sa, pl.f32, p->h_store_dtype, p->dk, dvt, s));
+      sa.gam = (const float*)(ws + pl.gam); sa.Wf = ws + pl.Wf; sa.KtTf = ws + pl.KtTf; sa.Ua = (const float*)(ws + pl.Ua);
+      sa.o = nullptr; sa.hs = ws + pl.hs;
+      if (p->cp_segments > 1) {
+        sa.summ = (float*)(ws + pl.summ); sa.hstart = (const float*)(ws + pl.hst);
+        GDR_LAUNCH(GDR_KERNEL_CP_SCAN_FWD, s, gdr::launch_scan_fwd(sa, pl.f32, p->h_store_dtype, p->dk, dvt_cp, 0, s));
+        gdr::CpChainArgs ca{geo, p->dk, p->dv, p->layout, 0, h0, (const float*)(ws + pl.summ), (float*)(ws + pl.hst)};
+        GDR_LAUNCH(GDR_KERNEL_CP_CHAIN_FWD, s, gdr::launch_cp_chain(ca, s));
+      }
+      GDR_LAUNCH(GDR_KERNEL_SCAN_FWD, s, gdr::launch_scan_fwd(sa, pl.f32, p->h_store_dtype, p->dk, dvt, 1, s));
     }
   }
   gdr::ScanBwdArgs ba{};
   ba.geo = geo; ba.DV = p->dv; ba.layout = p->layout; ba.dhT = dhT; ba.dh0 = dh0;
-  ba.gam = (const float*)(ws + pl.gam); ba.Ktf = ws + pl.Ktf; ba.PsTf = ws + pl.PsTf; ba.QgsTf = ws + pl.QgsTf;
-  ba.WTf = ws + pl.WTf; ba.dOf = ws + pl.dOf; ba.dhs = ws + pl.dhs; ba.dD = ws + pl.dD;
-  GDR_LAUNCH(GDR_KERNEL_SCAN_BWD, s, gdr::launch_scan_bwd(ba, pl.f32, p->dk, dvt, s));
+  ba.gam = (const float*)(ws + pl.gam); ba.Kf = ws + pl.Kf; ba.WTf = ws + pl.WTf;
+  ba.dDl = (const float*)(ws + pl.dDl); ba.Z = (const float*)(ws + pl.Z); ba.dhs = ws + pl.dhs; ba.dD = (float*)(ws + pl.dD);
+  if (p->cp_segments > 1) {
+    // the forward recompute above is done with the hand-off buffer: reuse it
+    ba.summ = (float*)(ws + pl.summ); ba.dhend = (const float*)(ws + pl.hst);
+    GDR_LAUNCH(GDR_KERNEL_CP_SCAN_BWD, s, gdr::launch_scan_bwd(ba, pl.f32, p->dk, dvt_cp, 0, s));
+    gdr::CpChainArgs ca{geo, p->dk, p->dv, p->layout, 1, dhT, (const float*)(ws + pl.summ), (float*)(ws + pl.hst)};
+    GDR_LAUNCH(GDR_KERNEL_CP_CHAIN_BWD, s, gdr::launch_cp_chain(ca, s));
+  }
+  GDR_LAUNCH(GDR_KERNEL_SCAN_BWD, s, gdr::launch_scan_bwd(ba, pl.f32, p->dk, dvt, 1, s));
   if (pl.NCb > 0) {
     gdr::GradArgs ga{};
     ga.geo = geo; ga.DV = p->dv; ga.scale = scale;
     ga.q = q; ga.k = k; ga.v = v; ga.dO = dO; ga.beta = beta;
-    ga.gam = (const float*)(ws + pl.gam); ga.Wf = ws + pl.Wf; ga.Ua = ws + pl.Ua; ga.Tm = (const float*)(ws + pl.Tm);
-    ga.hs = hs; ga.dhs = ws + pl.dhs; ga.dD = ws + pl.dD;
+    ga.gam = (const float*)(ws + pl.gam); ga.Wf = ws + pl.Wf; ga.Ua = (const float*)(ws + pl.Ua); ga.Tm = (const float*)(ws + pl.Tm);
+    ga.hs = hs; ga.dhs = ws + pl.dhs; ga.dD = (const float*)(ws + pl.dD);
     ga.dq = dq; ga.dk = dk; ga.dv = dv; ga.dbeta = dbeta; ga.dg = dg;
     GDR_LAUNCH(GDR_KERNEL_GRAD, s, gdr::launch_grad(ga, pl.f32, p->h_store_dtype, p->dk, s));
   }

@@ -33,17 +33,29 @@
 namespace gdr {
 
 // ---------------------------------------------------------------------------
-// k_scan_bwd: per (sequence, head, DV tile), chunks last to first.  dh (the
+// k_scan_bwd: per (unit, column tile), chunks last to first.  dh (the
 // gradient of the state at the chunk's end, DK x DVT fp32) lives in MFMA
-// accumulators; a bf16 copy dh^T in LDS is the B operand of K dh.  The
-// per-chunk operands that do not depend on dh (E K, scale P^T, scale Qg^T,
-// W^T, dO^T, e^{gamma_L}), all in fragment order, are loaded raw into a ring
-// of SCAN_STAGES register sets, SCAN_STAGES - 1 chunks ahead.  Writes the dh
-// snapshot and dDelta (accumulator order) and dh0.
+// accumulators; dh^T in LDS is a split operand (hi, lo) of K dh.  Per chunk
+//   dDelta = E (K dh) + scale P^T dO          (E scales rows; K exact)
+//   dh    <- e^{gamma_L} dh + scale Qg^T dO - W^T dDelta
+// where the two dh-independent terms come precomputed in fp32 and
+// -dDelta^T goes to LDS as a split operand.  The per-chunk operands (K,
+// W^T, the two fp32 terms, the gate factors) are loaded raw into a ring of
+// SCAN_STAGES register sets, SCAN_STAGES - 1 chunks ahead.  Writes the dh
+// snapshot (io dtype) and dDelta (fp32), both in accumulator order, and dh0.
+//   MODE 1: the reverse scan proper.
+//   MODE 0: CP segment summary -- scans the augmented gradient [I | 0] of
+//           width DK + DV backwards over one segment (the identity columns
+//           take no dO terms, so they evolve by the transposed transitions
+//           alone) and writes [prod M_c^T | gradient from zero] at the
+//           segment start.
+// A unit is a (sequence, CP segment, head); segments other than the last
+// start from the hand-off gradient, and only the first writes dh0.
 #define SCAN_STAGES 3
 
-template <typename T, int DK, int DVT>
+template <typename T, int DK, int DVT, int MODE>
 __global__ __launch_bounds__(256) void k_scan_bwd(const ScanBwdArgs a) {
+  constexpr bool SPLIT = sizeof(T) == 2;
   constexpr int P = pad_of<T>();
   constexpr int LDH = DK + P;
   constexpr int LDD = 64 + P;
@@ -54,17 +66,21 @@ __global__ __launch_bounds__(256) void k_scan_bwd(const ScanBwdArgs a) {
   constexpr int NT = DVT / 16;
   constexpr int S = sizeof(T) == 2 ? SCAN_STAGES : 2;  // fp32 fragments are 8x larger
   typedef typename Mma<T>::frag frag;
-  __shared__ __align__(16) T sDH[DVT * LDH];     // dh^T (dv, dk), operand copy
-  __shared__ __align__(16) T sDD[DVT * LDD];     // -dDelta^T (dv, r)
+  __shared__ __align__(16) T sDH[DVT * LDH];               // dh^T (dv, dk), hi
+  __shared__ __align__(16) T sDHl[SPLIT ? DVT * LDH : 1];  // lo
+  __shared__ __align__(16) T sDD[DVT * LDD];               // -dDelta^T (dv, r), hi
+  __shared__ __align__(16) T sDDl[SPLIT ? DVT * LDD : 1];  // lo
 
-  const int H = a.geo.H, DV = a.DV;
-  const int Pn = a.geo.N * H;
-  const int b = blockIdx.x;
-  const int jt = b / Pn, p = b - jt * Pn;
-  const int n = p / H, h = p - n * H;
-  const int dv0 = jt * DVT;
+  const int H = a.geo.H, DV = a.DV, CP = a.geo.cp, N = a.geo.N;
+  int p, jt;
+  if (!unit_of(blockIdx.x, N * CP * H, a.ntiles, p, jt)) return;
+  const int h = p % H, sg = (p / H) % CP, n = p / (H * CP);
+  if (MODE == 0 && sg == 0) return;        // the first segment hands nothing back
+  const int col0 = jt * DVT;
+  const bool mtile = MODE == 0 && col0 < DK;   // transition columns: start at I, no dO
+  const int dv0 = MODE == 0 ? (mtile ? 0 : col0 - DK) : col0;   // column of the dO terms
   int c0, nc, ts, tl;
-  seq_range(a.geo, n, c0, nc, ts, tl);
+  seg_range(a.geo, n, sg, c0, nc, ts, tl);
   const int w = wave_id();
   const int dkw = w * (DK / 4);
   const int rw = 16 * w;
@@ -72,6 +88,7 @@ __global__ __launch_bounds__(256) void k_scan_bwd(const ScanBwdArgs a) {
 
   f32x4 acc_h[MTH][NT];
   const int64_t sb = (int64_t)(n * H + h) * DK * DV;
+  const int64_t cpb = ((int64_t)sg * N * H + n * H + h) * DK;
 #pragma unroll
   for (int mt = 0; mt < MTH; ++mt)
 #pragma unroll
@@ -80,99 +97,98 @@ __global__ __launch_bounds__(256) void k_scan_bwd(const ScanBwdArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int dk = dkw + 16 * mt + acc_row0() + i, dv = dv0 + 16 * nt + acc_col();
         float v = 0.f;
-        if (a.dhT) v = (a.layout == 0) ? a.dhT[sb + (int64_t)dk * DV + dv] : a.dhT[sb + (int64_t)dv * DK + dk];
+        if (MODE == 0) v = (mtile && dk == col0 + 16 * nt + acc_col()) ? 1.f : 0.f;
+        else if (sg < CP - 1) v = a.dhend[(cpb + dk) * DV + dv];
+        else if (a.dhT) v = (a.layout == 0) ? a.dhT[sb + (int64_t)dk * DV + dv] : a.dhT[sb + (int64_t)dv * DK + dk];
         acc_h[mt][nt][i] = v;
       }
 #pragma unroll
   for (int mt = 0; mt < MTH; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) store_acc_t(sDH, LDH, dkw + 16 * mt, 16 * nt, acc_h[mt][nt]);
+    for (int nt = 0; nt < NT; ++nt) store_acc_t2(sDH, sDHl, LDH, dkw + 16 * mt, 16 * nt, acc_h[mt][nt]);
 
   struct Ops {
-    frag kf[KS];           // E K rows 16w (rows >= len are zero)
-    frag pf[KS64];         // scale P^T rows 16w
-    frag qf[MTH][KS64];    // scale Qg^T rows dkw..
-    frag wf[MTH][KS64];    // W^T rows dkw..
-    frag dof[NT][KS64];    // dO^T rows dv (B operand: k = chunk row, j = dv)
-    float eL;              // e^{gamma_L}
+    frag kf[KS];            // K rows 16w (rows >= len are zero)
+    frag wf[MTH][KS64];     // W^T rows dkw..
+    f32x4 dl[NT];           // scale P^T dO (fp32, accumulator order, raw)
+    f32x4 z[MTH][NT];       // scale Qg^T dO (fp32, accumulator order, raw)
+    f32x4 ee;               // e^{gamma_L - gamma} of the lane's 4 rows
+    float eL;               // e^{gamma_L}
   };
   auto load_ops = [&](int c, Ops& o) {
     const int64_t ch = chb + c;
-    const T* Kb = (const T*)a.Ktf + ch * 64 * DK;
+    const T* Kb = (const T*)a.Kf + ch * 64 * DK;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) o.kf[ks] = frag_af<T, DK>(Kb, w, ks);
-    const T* Pb = (const T*)a.PsTf + ch * 4096;
-#pragma unroll
-    for (int ks = 0; ks < KS64; ++ks) o.pf[ks] = frag_af<T, 64>(Pb, w, ks);
-    const T* Qb = (const T*)a.QgsTf + ch * DK * 64;
     const T* Wb = (const T*)a.WTf + ch * DK * 64;
 #pragma unroll
     for (int mt = 0; mt < MTH; ++mt)
 #pragma unroll
-      for (int ks = 0; ks < KS64; ++ks) {
-        o.qf[mt][ks] = frag_af<T, 64>(Qb, dkw / 16 + mt, ks);
-        o.wf[mt][ks] = frag_af<T, 64>(Wb, dkw / 16 + mt, ks);
-      }
-    const T* Db = (const T*)a.dOf + ch * DV * 64;
+      for (int ks = 0; ks < KS64; ++ks) o.wf[mt][ks] = frag_af<T, 64>(Wb, dkw / 16 + mt, ks);
+    const float* Db = a.dDl + ch * 64 * DV;
+    const float* Zb = a.Z + ch * DK * DV;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+    for (int nt = 0; nt < NT; ++nt) {
+      o.dl[nt] = *reinterpret_cast<const f32x4*>(Db + acc_off(w, dv0 / 16 + nt, DV));
 #pragma unroll
-      for (int ks = 0; ks < KS64; ++ks) o.dof[nt][ks] = frag_af<T, 64>(Db, dv0 / 16 + nt, ks);
-    o.eL = a.gam[ch * GSTRIDE + 64 + 63];
+      for (int mt = 0; mt < MTH; ++mt)
+        o.z[mt][nt] = *reinterpret_cast<const f32x4*>(Zb + acc_off(dkw / 16 + mt, dv0 / 16 + nt, DV));
+    }
+    const float* gb = a.gam + ch * GSTRIDE;
+    o.ee = *reinterpret_cast<const f32x4*>(gb + 128 + rw + acc_row0());
+    o.eL = gb[64 + 63];
   };
 
   auto process = [&](int c, Ops& o) {
     const int64_t ch = chb + c;
-    {
+    if constexpr (MODE != 0) {
       T* db = (T*)a.dhs + ch * DK * DV;
 #pragma unroll
       for (int mt = 0; mt < MTH; ++mt)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) store_acc4(db + acc_off(dkw / 16 + mt, dv0 / 16 + nt, DV), acc_h[mt][nt]);
     }
-    __syncthreads();
-    // dDelta = (E K) dh + scale P^T dO, rows 16w
+    __syncthreads();  // dh^T complete; last chunk's readers of dDelta^T are done
+    // dDelta = E (K dh) + scale P^T dO, rows 16w
     f32x4 acc_d[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc_d[nt] = zero4();
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc_d[nt] = Mma<T>::mma(o.kf[ks], frag_rowk(sDH, LDH, 16 * nt, ks * KW), acc_d[nt]);
-#pragma unroll
-    for (int ks = 0; ks < KS64; ++ks)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc_d[nt] = Mma<T>::mma(o.pf[ks], o.dof[nt][ks], acc_d[nt]);
-    {
-      T* ddb = (T*)a.dD + ch * 64 * DV;
-#pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        store_acc4(ddb + acc_off(w, dv0 / 16 + nt, DV), acc_d[nt]);
-        store_acc_t(sDD, LDD, rw, 16 * nt, -acc_d[nt]);
+        acc_d[nt] = Mma<T>::mma(o.kf[ks], frag_rowk(sDH, LDH, 16 * nt, ks * KW), acc_d[nt]);
+        if constexpr (SPLIT) acc_d[nt] = Mma<T>::mma(o.kf[ks], frag_rowk(sDHl, LDH, 16 * nt, ks * KW), acc_d[nt]);
       }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      acc_d[nt] = acc_d[nt] * o.ee + (mtile ? zero4() : o.dl[nt]);
+      if constexpr (MODE != 0) store_acc4(a.dD + ch * 64 * DV + acc_off(w, dv0 / 16 + nt, DV), acc_d[nt]);
+      store_acc_t2(sDD, sDDl, LDD, rw, 16 * nt, -acc_d[nt]);
     }
-    __syncthreads();
-    // dh <- e^{gamma_L} dh + (scale Qg)^T dO - W^T dDelta
+    __syncthreads();  // -dDelta^T complete; all readers of dh^T are done
+    // dh <- e^{gamma_L} dh + scale Qg^T dO - W^T dDelta
 #pragma unroll
     for (int mt = 0; mt < MTH; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc_h[mt][nt] *= o.eL;
+      for (int nt = 0; nt < NT; ++nt) acc_h[mt][nt] = acc_h[mt][nt] * o.eL + (mtile ? zero4() : o.z[mt][nt]);
 #pragma unroll
     for (int ks = 0; ks < KS64; ++ks)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const frag bo = o.dof[nt][ks];
         const frag bd = frag_rowk(sDD, LDD, 16 * nt, ks * KW);
 #pragma unroll
-        for (int mt = 0; mt < MTH; ++mt) {
-          acc_h[mt][nt] = Mma<T>::mma(o.qf[mt][ks], bo, acc_h[mt][nt]);
-          acc_h[mt][nt] = Mma<T>::mma(o.wf[mt][ks], bd, acc_h[mt][nt]);
+        for (int mt = 0; mt < MTH; ++mt) acc_h[mt][nt] = Mma<T>::mma(o.wf[mt][ks], bd, acc_h[mt][nt]);
+        if constexpr (SPLIT) {
+          const frag bdl = frag_rowk(sDDl, LDD, 16 * nt, ks * KW);
+#pragma unroll
+          for (int mt = 0; mt < MTH; ++mt) acc_h[mt][nt] = Mma<T>::mma(o.wf[mt][ks], bdl, acc_h[mt][nt]);
         }
       }
 #pragma unroll
     for (int mt = 0; mt < MTH; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) store_acc_t(sDH, LDH, dkw + 16 * mt, 16 * nt, acc_h[mt][nt]);
+      for (int nt = 0; nt < NT; ++nt) store_acc_t2(sDH, sDHl, LDH, dkw + 16 * mt, 16 * nt, acc_h[mt][nt]);
   };
 
   // Chunks are processed last to first: step j handles chunk nc - 1 - j and
@@ -196,7 +212,17 @@ __global__ __launch_bounds__(256) void k_scan_bwd(const ScanBwdArgs a) {
     for (int s = 0; s < S - 1; ++s)
       if (jb + s < nc) process(nc - 1 - (jb + s), st[s]);
   }
-  if (a.dh0) {
+  if (MODE == 0) {
+#pragma unroll
+    for (int mt = 0; mt < MTH; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int dk = dkw + 16 * mt + acc_row0() + i;
+          a.summ[(cpb + dk) * (DK + DV) + col0 + 16 * nt + acc_col()] = acc_h[mt][nt][i];
+        }
+  } else if (a.dh0 && sg == 0) {
 #pragma unroll
     for (int mt = 0; mt < MTH; ++mt)
 #pragma unroll
@@ -210,6 +236,10 @@ __global__ __launch_bounds__(256) void k_scan_bwd(const ScanBwdArgs a) {
   }
 }
 
+// value columns per phase-1 step of k_grad (keeps its LDS at two workgroups
+// per compute unit)
+#define GRAD_DVB 32
+
 // ---------------------------------------------------------------------------
 // k_grad: per (chunk, head).  Phase 1 loops over DV in blocks of DVB and
 // accumulates the DV-contracted products (dQg, dKt, dW, dP, dT_V) in
@@ -219,16 +249,17 @@ __global__ __launch_bounds__(256) void k_scan_bwd(const ScanBwdArgs a) {
 // reduced in a fixed order.
 template <typename T, typename HS, int DK>
 __global__ __launch_bounds__(256, 2) void k_grad(const GradArgs a) {
+  constexpr bool SPLIT = sizeof(T) == 2;
   constexpr int P = pad_of<T>();
   constexpr int LDK = DK + P;
   constexpr int L64 = 64 + P;
-  constexpr int DVB = dvb_of<T>();
+  constexpr int DVB = GRAD_DVB;
   constexpr int LDV = DVB + P;
   constexpr int KW = Mma<T>::KW;
   constexpr int NTK = DK / 16;
   constexpr int NTB = DVB / 16;
   typedef typename Mma<T>::frag frag;
-  constexpr int PH1 = (2 * DVB * LDK + 2 * DVB * L64 + 64 * LDV) * (int)sizeof(T);
+  constexpr int PH1 = (2 * DVB * LDK + 3 * DVB * L64 + 64 * LDV) * (int)sizeof(T);
   constexpr int PH2 = (2 * 64 * LDK + DK * L64 + 64 * L64) * (int)sizeof(T);
   extern __shared__ __align__(16) char smem[];
   T* sT = (T*)smem;                       // T (r, s), operand copy
@@ -242,8 +273,9 @@ __global__ __launch_bounds__(256, 2) void k_grad(const GradArgs a) {
   // phase 1
   T* sHvk = (T*)uni;                      // h rows (dv, dk)
   T* sDHvk = sHvk + DVB * LDK;            // dh rows (dv, dk)
-  T* sDeltaT = sDHvk + DVB * LDK;         // Delta^T (dv, r)
-  T* sDDt = sDeltaT + DVB * L64;          // dDelta^T (dv, r)
+  T* sDeltaT = sDHvk + DVB * LDK;         // Delta^T (dv, r), hi
+  T* sDeltaTl = sDeltaT + DVB * L64;      // lo
+  T* sDDt = sDeltaTl + DVB * L64;         // dDelta^T (dv, r)
   T* sV = sDDt + DVB * L64;               // V (r, dv)
   // phase 2 (aliases phase 1)
   T* sQ = (T*)uni;                        // Q (r, dk); later dT^T (s, r)
@@ -313,7 +345,7 @@ __global__ __launch_bounds__(256, 2) void k_grad(const GradArgs a) {
         store_acc4(sHvk + dvl * LDK + dk, hv);
         store_acc4(sDHvk + dvl * LDK + dk, gv);
       }
-      const T* ddb = (const T*)a.dD + ch * 64 * DV;
+      const float* ddb = a.dD + ch * 64 * DV;
       for (int e = tid; e < 4 * NTB * 64; e += 256) {
         const int ll = e & 63, tt = e >> 6;
         const int m = tt / NTB, nn = tt - m * NTB;
@@ -326,7 +358,7 @@ __global__ __launch_bounds__(256, 2) void k_grad(const GradArgs a) {
     // Delta block = U - W h  (rows 16w)
     f32x4 aD[NTB];
     {
-      const T* Ub = (const T*)a.Ua + ch * 64 * DV;
+      const float* Ub = a.Ua + ch * 64 * DV;
 #pragma unroll
       for (int nt = 0; nt < NTB; ++nt) aD[nt] = load4f(Ub + acc_off(w, dvb / 16 + nt, DV));
 #pragma unroll
@@ -335,7 +367,7 @@ __global__ __launch_bounds__(256, 2) void k_grad(const GradArgs a) {
         for (int nt = 0; nt < NTB; ++nt)
           aD[nt] = Mma<T>::mma(wf[ks], frag_rowk(sHvk, LDK, 16 * nt, ks * KW), aD[nt]);
 #pragma unroll
-      for (int nt = 0; nt < NTB; ++nt) store_acc_t(sDeltaT, L64, rw, 16 * nt, aD[nt]);
+      for (int nt = 0; nt < NTB; ++nt) store_acc_t2(sDeltaT, sDeltaTl, L64, rw, 16 * nt, aD[nt]);
     }
     // dO fragments (rows 16w, k = dv)
     frag dof[DVB / KW];
@@ -357,14 +389,23 @@ __global__ __launch_bounds__(256, 2) void k_grad(const GradArgs a) {
       for (int nt = 0; nt < 4; ++nt) aTV[nt] = Mma<T>::mma(ddp, frag_rowk(sV, LDV, 16 * nt, ks * KW), aTV[nt]);
     }
     __syncthreads();  // Delta^T complete
-    // dKt += Delta dh^T ; dP += dO Delta^T
+    // dKt += Delta dh^T ; dP += dO Delta^T  (Delta split)
 #pragma unroll
     for (int ks = 0; ks < DVB / KW; ++ks) {
       const frag ad = frag_colk_lds(sDeltaT, L64, rw, ks * KW);
+      frag adl;
+      if constexpr (SPLIT) adl = frag_colk_lds(sDeltaTl, L64, rw, ks * KW);
 #pragma unroll
-      for (int nt = 0; nt < NTK; ++nt) aKt[nt] = Mma<T>::mma(ad, frag_colk_lds(sDHvk, LDK, 16 * nt, ks * KW), aKt[nt]);
+      for (int nt = 0; nt < NTK; ++nt) {
+        const frag bdh = frag_colk_lds(sDHvk, LDK, 16 * nt, ks * KW);
+        aKt[nt] = Mma<T>::mma(ad, bdh, aKt[nt]);
+        if constexpr (SPLIT) aKt[nt] = Mma<T>::mma(adl, bdh, aKt[nt]);
+      }
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) aP[nt] = Mma<T>::mma(dof[ks], frag_colk_lds(sDeltaT, L64, 16 * nt, ks * KW), aP[nt]);
+      for (int nt = 0; nt < 4; ++nt) {
+        aP[nt] = Mma<T>::mma(dof[ks], frag_colk_lds(sDeltaT, L64, 16 * nt, ks * KW), aP[nt]);
+        if constexpr (SPLIT) aP[nt] = Mma<T>::mma(dof[ks], frag_colk_lds(sDeltaTl, L64, 16 * nt, ks * KW), aP[nt]);
+      }
     }
     // dVb = T^T dDelta (rows s = 16w): dv = beta dVb, dbeta += rowsum(V dVb)
     {
@@ -661,26 +702,38 @@ __global__ __launch_bounds__(256, 2) void k_grad(const GradArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-template <typename T, int DK>
-static hipError_t launch_scan_bwd_t(const ScanBwdArgs& a, int dvt, hipStream_t st) {
-  const int grid = a.geo.N * a.geo.H * (a.DV / dvt);
-  if (grid == 0) return hipSuccess;
-  if (dvt == 16) hipLaunchKernelGGL((k_scan_bwd<T, DK, 16>), dim3(grid), dim3(256), 0, st, a);
-  else if (dvt == 32) hipLaunchKernelGGL((k_scan_bwd<T, DK, 32>), dim3(grid), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((k_scan_bwd<T, DK, 64>), dim3(grid), dim3(256), 0, st, a);
+template <typename T, int DK, int MODE>
+static hipError_t launch_scan_bwd_t(ScanBwdArgs a, int dvt, hipStream_t st) {
+  const int units = a.geo.N * a.geo.cp * a.geo.H;
+  a.ntiles = ((MODE == 0 ? DK : 0) + a.DV) / dvt;
+  const int grid = 8 * ((units + 7) / 8) * a.ntiles;
+  if (units == 0) return hipSuccess;
+  if (dvt == 16) hipLaunchKernelGGL((k_scan_bwd<T, DK, 16, MODE>), dim3(grid), dim3(256), 0, st, a);
+  else if constexpr (sizeof(T) == 2) {
+    if (dvt == 32) hipLaunchKernelGGL((k_scan_bwd<T, DK, 32, MODE>), dim3(grid), dim3(256), 0, st, a);
+    else if constexpr (DK == 64) hipLaunchKernelGGL((k_scan_bwd<T, DK, 64, MODE>), dim3(grid), dim3(256), 0, st, a);
+    else return hipErrorInvalidValue;
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_scan_bwd(const ScanBwdArgs& a, bool f32, int DK, int dvt, hipStream_t st) {
-  if (f32) return DK == 64 ? launch_scan_bwd_t<float, 64>(a, dvt, st) : launch_scan_bwd_t<float, 128>(a, dvt, st);
-  return DK == 64 ? launch_scan_bwd_t<bf16, 64>(a, dvt, st) : launch_scan_bwd_t<bf16, 128>(a, dvt, st);
+template <typename T, int DK>
+static hipError_t launch_scan_bwd_m(const ScanBwdArgs& a, int dvt, int mode, hipStream_t st) {
+  return mode == 0 ? launch_scan_bwd_t<T, DK, 0>(a, dvt, st) : launch_scan_bwd_t<T, DK, 1>(a, dvt, st);
+}
+
+hipError_t launch_scan_bwd(const ScanBwdArgs& a, bool f32, int DK, int dvt, int mode, hipStream_t st) {
+  if (f32) return DK == 64 ? launch_scan_bwd_m<float, 64>(a, dvt, mode, st) : launch_scan_bwd_m<float, 128>(a, dvt, mode, st);
+  return DK == 64 ? launch_scan_bwd_m<bf16, 64>(a, dvt, mode, st) : launch_scan_bwd_m<bf16, 128>(a, dvt, mode, st);
 }
 
 template <typename T, int DK>
 static size_t grad_smem() {
   constexpr int P = pad_of<T>();
-  constexpr int LDK = DK + P, L64 = 64 + P, DVB = dvb_of<T>(), LDV = DVB + P;
-  constexpr int PH1 = (2 * DVB * LDK + 2 * DVB * L64 + 64 * LDV) * (int)sizeof(T);
+  constexpr int LDK = DK + P, L64 = 64 + P, DVB = GRAD_DVB, LDV = DVB + P;
+  constexpr int PH1 = (2 * DVB * LDK + 3 * DVB * L64 + 64 * LDV) * (int)sizeof(T);
   constexpr int PH2 = (2 * 64 * LDK + DK * L64 + 64 * L64) * (int)sizeof(T);
   return 64 * L64 * sizeof(T) + (4 * 64 + 2 * 4 * 64 + 8) * 4 + cmax(PH1, PH2);
 }

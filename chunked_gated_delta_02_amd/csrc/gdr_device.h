@@ -177,6 +177,82 @@ __device__ __forceinline__ void store_acc_t(T* dst, int ld, int r0, int c0, f32x
   }
 }
 
+// Split operands.  An fp32 value x is carried as bf16 hi = RNE(x) plus
+// bf16 lo = RNE(x - hi); an MFMA product with a split operand is taken as
+// hi * b + lo * b, which keeps about 16 significant bits of x instead of 8.
+// On the fp32 path (T = float) there is no split: lo is never formed or used.
+template <typename T>
+__device__ __forceinline__ void split2(float x, T& hi, T& lo) {
+  hi = from_f32<T>(x);
+  lo = from_f32<T>(x - to_f32(hi));
+}
+
+// store_acc_t of a split tile: hi into dh, lo into dl (dl unused for fp32)
+template <typename T>
+__device__ __forceinline__ void store_acc_t2(T* dh, T* dl, int ld, int r0, int c0, f32x4 v) {
+  if constexpr (sizeof(T) == 2) {
+    typedef T t4 __attribute__((ext_vector_type(4)));
+    t4 h4, l4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      T hi, lo;
+      split2<T>(v[i], hi, lo);
+      h4[i] = hi;
+      l4[i] = lo;
+    }
+    const int64_t off = (int64_t)(c0 + acc_col()) * ld + r0 + acc_row0();
+    *reinterpret_cast<t4*>(dh + off) = h4;
+    *reinterpret_cast<t4*>(dl + off) = l4;
+  } else {
+    store_acc_t(dh, ld, r0, c0, v);
+  }
+}
+
+// RowK fragment of the fp32 LDS matrix x(i, k) = p[i * ld + k] * sk(k),
+// split into hi and lo (bf16) or taken as is (fp32).  p rows 16-byte aligned.
+template <typename T, typename SK>
+__device__ __forceinline__ void frag_rowk_f32(const float* p, int ld, int i0, int k0, SK&& sk,
+                                              typename Mma<T>::frag& hi, typename Mma<T>::frag& lo) {
+  const int l = lane_id();
+  if constexpr (Mma<T>::KPL == 8) {
+    const int kb = k0 + 8 * (l >> 4);
+    const float* q = p + (i0 + (l & 15)) * ld + kb;
+    const f32x4 a = *reinterpret_cast<const f32x4*>(q);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(q + 4);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      bf16 h, lw;
+      split2<bf16>((j < 4 ? a[j] : b[j - 4]) * sk(kb + j), h, lw);
+      hi[j] = h;
+      lo[j] = lw;
+    }
+  } else {
+    const int k = k0 + (l >> 4);
+    hi = p[(i0 + (l & 15)) * ld + k] * sk(k);
+  }
+}
+
+// ColK fragment of the 16-bit LDS matrix x(i, k) = p[k * ld + i] * sk(k),
+// split into hi and lo (fp32: taken as is).
+template <typename T, typename SK>
+__device__ __forceinline__ void frag_colk_scaled(const T* p, int ld, int i0, int k0, SK&& sk,
+                                                 typename Mma<T>::frag& hi, typename Mma<T>::frag& lo) {
+  const typename Mma<T>::frag raw = frag_colk_lds(p, ld, i0, k0);
+  const int l = lane_id();
+  if constexpr (Mma<T>::KPL == 8) {
+    const int kb = k0 + 8 * (l >> 4);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      bf16 h, lw;
+      split2<bf16>((float)raw[j] * sk(kb + j), h, lw);
+      hi[j] = h;
+      lo[j] = lw;
+    }
+  } else {
+    hi = raw * sk(k0 + (l >> 4));
+  }
+}
+
 // Store / load an accumulator tile in accumulator order (4 contiguous
 // elements per lane: 8-byte or 16-byte accesses, 64 lanes contiguous).
 template <typename T>
@@ -252,6 +328,7 @@ struct Geo {
   const int* cu;        // packed: cu_seqlens [N+1], else nullptr
   const int* seq_chunk; // packed: [N+1]
   const int* chunk_seq; // packed: [nchunks]
+  int cp;               // intra-card context-parallel segments per sequence (>= 1)
 };
 
 __device__ __forceinline__ bool chunk_lookup(const Geo& g, int ci, int& n, int& t0, int& len) {
@@ -289,6 +366,31 @@ __device__ __forceinline__ void seq_range(const Geo& g, int n, int& c0, int& nc,
     tl = min(max(g.cu[n + 1], ts), g.T_total) - ts;
     nc = min(nc, (tl + CH - 1) / CH);
   }
+}
+
+// chunk slots [c0, c0 + nc) and tokens [ts, ts + tl) of context-parallel
+// segment s of sequence n: segments hold ceil(chunks / cp) chunks each, the
+// trailing ones may be short or empty
+__device__ __forceinline__ void seg_range(const Geo& g, int n, int s, int& c0, int& nc, int& ts, int& tl) {
+  seq_range(g, n, c0, nc, ts, tl);
+  const int per = (nc + g.cp - 1) / g.cp;
+  const int b = min(s * per, nc), e = min(b + per, nc);
+  c0 += b;
+  nc = e - b;
+  ts += b * CH;
+  tl = max(0, min(tl - b * CH, nc * CH));
+}
+
+// XCD-aware placement of the serial-scan workgroups.  Workgroups are handed
+// to the 8 XCDs in turn (workgroup b runs on XCD b % 8), so unit p gets all
+// its column tiles on XCD p % 8: the tiles read the same chunk operands and
+// share them in that XCD's L2.  The grid is 8 * ceil(units / 8) * ntiles;
+// returns false for the padding workgroups.
+__device__ __forceinline__ bool unit_of(int b, int units, int ntiles, int& p, int& jt) {
+  const int x = b & 7, k = b >> 3;
+  jt = k % ntiles;
+  p = (k / ntiles) * 8 + x;
+  return p < units;
 }
 
 }  // namespace gdr

@@ -91,32 +91,35 @@ __global__ __launch_bounds__(1024) void k_plan(const int* cu, int N, int T_total
 // k_wy: per (chunk, head).  Computes gamma, A, T = (I + A)^-1 (blocked:
 // 16 x 16 diagonal blocks by forward substitution, then off-diagonal block
 // rows T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj on fp32 MFMA), W and U on the
-// operand-type MFMA, and P = Q K^T * Gam; writes everything the scans and
-// the gradient kernel consume, in fragment / accumulator order (see
-// gdr_kernels.h).
+// operand-type MFMA with T (fp32 in LDS) taken as a split operand, and
+// P = Q K^T * Gam; writes everything the scans and the gradient kernel
+// consume, in fragment / accumulator order (see gdr_kernels.h).
+//   forward:  W, U (fp32), K^T, Q, P (hi + lo)
+//   backward: W, U, T, W^T, K, scale P^T dO and scale (e^gamma Q)^T dO (fp32)
+//             (+ K^T when the forward states are recomputed)
+// LDS: sK | RA = {A fp32, then W, then Q} | RT = {T fp32, then P^T fp32} |
+//      sV (V / dO block) | sX | gate vectors.
 template <typename T, int DK, bool BWD>
 __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
   constexpr int P = pad_of<T>();
   constexpr int LDK = DK + P;
-  constexpr int L64 = 64 + P;
-  constexpr int LDF = 68;
+  constexpr int LDF = 68;   // fp32 64-wide tiles (16-byte aligned rows)
   constexpr int DVB = dvb_of<T>();
   constexpr int LDV = DVB + P;
   constexpr int KW = Mma<T>::KW;
-  constexpr int R1 = cmax(cmax(2 * 64 * LDF * 4, (64 * LDK + 64 * LDV) * (int)sizeof(T)),
-                          (64 * LDK + 64 * L64) * (int)sizeof(T));
+  constexpr bool SPLIT = sizeof(T) == 2;
+  constexpr int RA = cmax(64 * LDF * 4, 64 * LDK * (int)sizeof(T));
+  typedef typename Mma<T>::frag frag;
   extern __shared__ __align__(16) char smem[];
   T* sK = (T*)smem;
-  char* r1 = smem + 64 * LDK * sizeof(T);
-  float* sA = (float*)r1;              // A (fp32), then dead
-  float* sTm = sA + 64 * LDF;          // T (fp32), then dead
-  T* sW = (T*)r1;                      // W (r, dk), after T1/T2 are built
-  T* sV = sW + 64 * LDK;               // V / dO block (r, dv)
-  T* sQ = (T*)r1;                      // Q (r, dk), after W and V are done
-  T* sP = sQ + 64 * LDK;               // P (r, s)
-  T* sT1 = (T*)(r1 + R1);
-  T* sT2 = sT1 + 64 * L64;
-  float* sX = (float*)(sT2 + 64 * L64);
+  char* ra = smem + 64 * LDK * sizeof(T);
+  float* sA = (float*)ra;                 // A (fp32), until T is built
+  T* sW = (T*)ra;                         // W (r, dk) staging
+  T* sQ = (T*)ra;                         // Q (r, dk), after W is written
+  float* sTm = (float*)(ra + RA);         // T (fp32), until U is done
+  float* sPT = sTm;                       // then P^T (s, r) fp32
+  T* sV = (T*)(ra + RA + 64 * LDF * 4);   // V / dO block (r, dv)
+  float* sX = (float*)(sV + 64 * LDV);
   float* sg = sX + 4 * 16 * 20;
   float* sb = sg + 64;
   float* seg = sb + 64;
@@ -130,6 +133,7 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
   const int64_t ch = (int64_t)h * a.geo.nchunks + ci;
   const T* kp = (const T*)a.k;
   const T* vp = (const T*)a.v;
+  const int64_t rowq = (int64_t)t0 * H + h;   // token-row index of chunk row 0
 
   if (w == 0) {
     float gv = 0.f, bv = 0.f;
@@ -148,7 +152,7 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
     a.gam[ch * GSTRIDE + 64 + l] = eg;
     a.gam[ch * GSTRIDE + 128 + l] = eE;
   }
-  load_rows<T, DK>(sK, LDK, kp + ((int64_t)t0 * H + h) * DK, (int64_t)H * DK, len);
+  load_rows<T, DK>(sK, LDK, kp + rowq * DK, (int64_t)H * DK, len);
   __syncthreads();
 
   // A = strictly_lower(diag(beta) K K^T * Gam): rows 16w, 4 column tiles
@@ -220,19 +224,14 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
     }
     __syncthreads();
   }
-
-  // T1 = T diag(beta e^gamma), T2 = T diag(beta) in the operand type
-  for (int e = tid; e < 64 * 64; e += 256) {
-    const int r = e >> 6, s = e & 63;
-    const float t = sTm[r * LDF + s];
-    sT1[r * L64 + s] = from_f32<T>(t * sb[s] * seg[s]);
-    sT2[r * L64 + s] = from_f32<T>(t * sb[s]);
-    if constexpr (BWD) a.Tm[ch * 4096 + e] = t;
+  if constexpr (BWD) {
+    for (int e = tid; e < 64 * 64; e += 256) a.Tm[ch * 4096 + e] = sTm[(e >> 6) * LDF + (e & 63)];
   }
-  __syncthreads();  // sA / sTm are dead from here
 
-  // W^T = K^T T1^T (DK x 64): wave w owns dk rows [w DK/4, (w+1) DK/4);
-  // staged row-major in LDS, then written out in fragment order
+  // W^T = K^T (T diag(beta e^gamma))^T (DK x 64): wave w owns dk rows
+  // [w DK/4, (w+1) DK/4); T diag(beta e^gamma) is a split operand read from
+  // the fp32 T.  Staged row-major in LDS (over A, which is dead), then
+  // written out in fragment order.
   {
     constexpr int MT = DK / 64;
     f32x4 acc[MT][4];
@@ -240,16 +239,21 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = zero4();
+    auto d1 = [&](int s) { return sb[s] * seg[s]; };
 #pragma unroll
     for (int ks = 0; ks < 64; ks += KW) {
-      typename Mma<T>::frag af[MT];
+      frag af[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) af[mt] = frag_colk_lds(sK, LDK, w * (DK / 4) + 16 * mt, ks);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const auto bf = frag_rowk(sT1, L64, 16 * nt, ks);
+        frag bh, bl;
+        frag_rowk_f32<T>(sTm, LDF, 16 * nt, ks, d1, bh, bl);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt][nt] = Mma<T>::mma(af[mt], bf, acc[mt][nt]);
+        for (int mt = 0; mt < MT; ++mt) {
+          acc[mt][nt] = Mma<T>::mma(af[mt], bh, acc[mt][nt]);
+          if constexpr (SPLIT) acc[mt][nt] = Mma<T>::mma(af[mt], bl, acc[mt][nt]);
+        }
       }
     }
 #pragma unroll
@@ -261,47 +265,43 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
   write_afrag<T, 64, DK>((T*)a.Wf + ch * 64 * DK, [&](int i, int k) { return to_f32(sW[i * LDK + k]); });
   if constexpr (BWD) {
     write_afrag<T, DK, 64>((T*)a.WTf + ch * DK * 64, [&](int i, int k) { return to_f32(sW[k * LDK + i]); });
-    write_afrag<T, 64, DK>((T*)a.Ktf + ch * 64 * DK, [&](int i, int k) { return sE[i] * to_f32(sK[i * LDK + k]); });
+    write_afrag<T, 64, DK>((T*)a.Kf + ch * 64 * DK, [&](int i, int k) { return to_f32(sK[i * LDK + k]); });
   }
   if (a.KtTf)
-    write_afrag<T, DK, 64>((T*)a.KtTf + ch * DK * 64, [&](int i, int k) { return sE[k] * to_f32(sK[k * LDK + i]); });
+    write_afrag<T, DK, 64>((T*)a.KtTf + ch * DK * 64, [&](int i, int k) { return to_f32(sK[k * LDK + i]); });
 
-  // U = T2 V per DV block (rows 16w), written in accumulator order
-  for (int dv0 = 0; dv0 < DV; dv0 += DVB) {
-    __syncthreads();
-    load_rows<T, DVB>(sV, LDV, vp + ((int64_t)t0 * H + h) * DV + dv0, (int64_t)H * DV, len);
-    __syncthreads();
-    f32x4 acc[DVB / 16];
-#pragma unroll
-    for (int nt = 0; nt < DVB / 16; ++nt) acc[nt] = zero4();
-#pragma unroll
-    for (int ks = 0; ks < 64; ks += KW) {
-      const auto af = frag_rowk(sT2, L64, 16 * w, ks);
-#pragma unroll
-      for (int nt = 0; nt < DVB / 16; ++nt)
-        acc[nt] = Mma<T>::mma(af, frag_colk_lds(sV, LDV, 16 * nt, ks), acc[nt]);
-    }
-    T* Ub = (T*)a.Ua + ch * 64 * DV;
-#pragma unroll
-    for (int nt = 0; nt < DVB / 16; ++nt) store_acc4(Ub + acc_off(w, dv0 / 16 + nt, DV), acc[nt]);
-  }
-  if constexpr (BWD) {
-    // dO^T in fragment order, per DV block
-    const T* dop = (const T*)a.dO;
+  // U = T diag(beta) V per DV block (rows 16w, fp32, accumulator order);
+  // T diag(beta) is a split operand read from the fp32 T
+  {
+    auto d2 = [&](int s) { return sb[s]; };
     for (int dv0 = 0; dv0 < DV; dv0 += DVB) {
       __syncthreads();
-      load_rows<T, DVB>(sV, LDV, dop + ((int64_t)t0 * H + h) * DV + dv0, (int64_t)H * DV, len);
+      load_rows<T, DVB>(sV, LDV, vp + rowq * DV + dv0, (int64_t)H * DV, len);
       __syncthreads();
-      write_afrag<T, DVB, 64>((T*)a.dOf + ch * DV * 64 + (int64_t)dv0 * 64,
-                              [&](int i, int k) { return to_f32(sV[k * LDV + i]); });
+      f32x4 acc[DVB / 16];
+#pragma unroll
+      for (int nt = 0; nt < DVB / 16; ++nt) acc[nt] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < 64; ks += KW) {
+        frag ah, al;
+        frag_rowk_f32<T>(sTm, LDF, 16 * w, ks, d2, ah, al);
+#pragma unroll
+        for (int nt = 0; nt < DVB / 16; ++nt) {
+          const frag bv = frag_colk_lds(sV, LDV, 16 * nt, ks);
+          acc[nt] = Mma<T>::mma(ah, bv, acc[nt]);
+          if constexpr (SPLIT) acc[nt] = Mma<T>::mma(al, bv, acc[nt]);
+        }
+      }
+      float* Ub = a.Ua + ch * 64 * DV;
+#pragma unroll
+      for (int nt = 0; nt < DVB / 16; ++nt) store_acc4(Ub + acc_off(w, dv0 / 16 + nt, DV), acc[nt]);
     }
   }
 
-  __syncthreads();  // sW / sV are dead from here
-  load_rows<T, DK>(sQ, LDK, (const T*)a.q + ((int64_t)t0 * H + h) * DK, (int64_t)H * DK, len);
+  __syncthreads();  // W staging, T and V are dead from here
+  load_rows<T, DK>(sQ, LDK, (const T*)a.q + rowq * DK, (int64_t)H * DK, len);
   __syncthreads();
-  // P = Q K^T * Gam (diagonal included), computed as P^T (rows s = 16w),
-  // staged row-major (r, s) in LDS
+  // P^T = K Q^T * Gam^T (rows s = 16w, diagonal included), staged fp32
   {
     f32x4 acc[4];
 #pragma unroll
@@ -319,37 +319,89 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
         const int s = 16 * w + acc_row0() + i, r = 16 * nt + acc_col();
         acc[nt][i] = (s <= r) ? acc[nt][i] * expf(sg[r] - sg[s]) : 0.f;
       }
-      store_acc_t(sP, L64, 16 * w, 16 * nt, acc[nt]);
+      store_acc(sPT, LDF, 16 * w, 16 * nt, acc[nt]);
     }
   }
   __syncthreads();
   if constexpr (!BWD) {
-    write_afrag<T, 64, 64>((T*)a.Pf + ch * 4096, [&](int i, int k) { return to_f32(sP[i * L64 + k]); });
-    write_afrag<T, 64, DK>((T*)a.Qgf + ch * 64 * DK, [&](int i, int k) { return seg[i] * to_f32(sQ[i * LDK + k]); });
+    write_afrag<T, 64, 64>((T*)a.Pf + ch * 4096, [&](int i, int k) { return sPT[k * LDF + i]; },
+                           SPLIT ? (T*)a.Pfl + ch * 4096 : nullptr);
+    write_afrag<T, 64, DK>((T*)a.Qf + ch * 64 * DK, [&](int i, int k) { return to_f32(sQ[i * LDK + k]); });
   } else {
+    // per DV block of dO: scale P^T dO (rows s = 16w) and scale Qg^T dO
+    // (rows dk: wave w owns [w DK/4, (w+1) DK/4)), fp32, accumulator order;
+    // P^T and Qg^T are split operands
     const float sc = a.scale;
-    write_afrag<T, 64, 64>((T*)a.PsTf + ch * 4096, [&](int i, int k) { return sc * to_f32(sP[k * L64 + i]); });
-    write_afrag<T, DK, 64>((T*)a.QgsTf + ch * DK * 64,
-                           [&](int i, int k) { return sc * seg[k] * to_f32(sQ[k * LDK + i]); });
+    const T* dop = (const T*)a.dO;
+    auto ps = [&](int) { return sc; };
+    auto qs = [&](int r) { return sc * seg[r]; };
+    constexpr int MT = DK / 64;
+    for (int dv0 = 0; dv0 < DV; dv0 += DVB) {
+      __syncthreads();
+      load_rows<T, DVB>(sV, LDV, dop + rowq * DV + dv0, (int64_t)H * DV, len);
+      __syncthreads();
+      f32x4 accp[DVB / 16], accz[MT][DVB / 16];
+#pragma unroll
+      for (int nt = 0; nt < DVB / 16; ++nt) {
+        accp[nt] = zero4();
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) accz[mt][nt] = zero4();
+      }
+#pragma unroll
+      for (int ks = 0; ks < 64; ks += KW) {
+        frag ph, pl, qh[MT], ql[MT];
+        frag_rowk_f32<T>(sPT, LDF, 16 * w, ks, ps, ph, pl);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) frag_colk_scaled<T>(sQ, LDK, w * (DK / 4) + 16 * mt, ks, qs, qh[mt], ql[mt]);
+#pragma unroll
+        for (int nt = 0; nt < DVB / 16; ++nt) {
+          const frag bo = frag_colk_lds(sV, LDV, 16 * nt, ks);
+          accp[nt] = Mma<T>::mma(ph, bo, accp[nt]);
+          if constexpr (SPLIT) accp[nt] = Mma<T>::mma(pl, bo, accp[nt]);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            accz[mt][nt] = Mma<T>::mma(qh[mt], bo, accz[mt][nt]);
+            if constexpr (SPLIT) accz[mt][nt] = Mma<T>::mma(ql[mt], bo, accz[mt][nt]);
+          }
+        }
+      }
+      float* Db = a.dDl + ch * 64 * DV;
+      float* Zb = a.Z + ch * DK * DV;
+#pragma unroll
+      for (int nt = 0; nt < DVB / 16; ++nt) {
+        store_acc4(Db + acc_off(w, dv0 / 16 + nt, DV), accp[nt]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) store_acc4(Zb + acc_off(w * MT + mt, dv0 / 16 + nt, DV), accz[mt][nt]);
+      }
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// k_scan_fwd: per (sequence, head, DV tile).  Serial over the sequence's
-// chunks.  The state tile h (DK x DVT, fp32) is held in MFMA accumulators
-// (wave w owns dk rows [w DK/4, (w+1) DK/4)); a bf16 copy h^T lives in LDS
-// as the B operand of W h (and of Q h for the output).  Delta^T goes to LDS
-// as the B operand of the update h <- e^{gamma_L} h + Kt^T Delta and of
-// P Delta.  All per-chunk operands that do not depend on h (W, Kt^T, U, Q,
-// P, the gate exponentials) are loaded raw into a ring of SCAN_STAGES
-// register sets, SCAN_STAGES - 1 chunks ahead; nothing touches a loaded
-// value before its chunk is processed, so the loads stay in flight while
-// earlier chunks run.  With OUT the kernel also writes
-// o = scale (e^gamma Q h + P Delta).
+// k_scan_fwd: per (unit, column tile).  Serial over the unit's chunks.  The
+// state tile h (DK x DVT, fp32) is held in MFMA accumulators (wave w owns dk
+// rows [w DK/4, (w+1) DK/4)); h^T lives in LDS as a split operand (hi, lo)
+// for W h and Q h.  Delta = U - W h and E Delta (E = e^{gamma_L - gamma})
+// go to LDS as split operands of P Delta and of the update
+// h <- e^{gamma_L} h + K^T (E Delta).  All per-chunk operands that do not
+// depend on h (W, K^T, U, Q, P, the gate factors) are loaded raw into a ring
+// of SCAN_STAGES register sets, SCAN_STAGES - 1 chunks ahead; nothing
+// touches a loaded value before its chunk is processed, so the loads stay in
+// flight while earlier chunks run.
+//   MODE 2: writes the snapshots and o = scale (e^gamma (Q h) + P Delta);
+//   MODE 1: writes the snapshots only (backward recompute);
+//   MODE 0: CP segment summary -- scans the augmented state [I | 0] of width
+//           DK + DV over one segment (the identity columns take U = 0, so
+//           they evolve by the chunk transitions M_c alone) and writes the
+//           final [prod M_c | state from zero] to the summary buffer.
+// A unit is a (sequence, CP segment, head); segments other than the first
+// start from the hand-off state, and only the last writes h_T.
 #define SCAN_STAGES 3
 
-template <typename T, typename HS, int DK, int DVT, bool OUT>
+template <typename T, typename HS, int DK, int DVT, int MODE>
 __global__ __launch_bounds__(256) void k_scan_fwd(const ScanFwdArgs a) {
+  constexpr bool OUT = MODE == 2;
+  constexpr bool SPLIT = sizeof(T) == 2;
   constexpr int P = pad_of<T>();
   constexpr int LDH = DK + P;
   constexpr int LDD = 64 + P;
@@ -358,22 +410,29 @@ __global__ __launch_bounds__(256) void k_scan_fwd(const ScanFwdArgs a) {
   constexpr int KS64 = 64 / KW;
   constexpr int MTH = DK / 64;
   constexpr int NT = DVT / 16;
-  constexpr int S = sizeof(T) == 2 ? SCAN_STAGES : 2;  // fp32 fragments are 8x larger
+  // ring depth: fp32 fragments are 8x larger, and the output operands of
+  // MODE 2 double the per-chunk set
+  constexpr int S = sizeof(T) == 2 ? (MODE != 2 ? SCAN_STAGES : 2) : (MODE != 2 ? 2 : 1);
   typedef typename Mma<T>::frag frag;
-  typedef T t4 __attribute__((ext_vector_type(4)));
   constexpr int LDO = DVT + P;
-  __shared__ __align__(16) T sH[DVT * LDH];
-  __shared__ __align__(16) T sD[DVT * LDD];
-  __shared__ __align__(16) T sO[OUT ? 64 * LDO : 1];  // output staging (each wave: its rows)
+  __shared__ __align__(16) T sH[DVT * LDH];                   // h^T (dv, dk), hi
+  __shared__ __align__(16) T sHl[SPLIT ? DVT * LDH : 1];      // lo
+  __shared__ __align__(16) T sDE[DVT * LDD];                  // (E Delta)^T (dv, r), hi
+  __shared__ __align__(16) T sDEl[SPLIT ? DVT * LDD : 1];
+  __shared__ __align__(16) T sD[OUT ? DVT * LDD : 1];         // Delta^T (dv, r), hi
+  __shared__ __align__(16) T sDl[OUT && SPLIT ? DVT * LDD : 1];
+  __shared__ __align__(16) T sO[OUT ? 64 * LDO : 1];          // output staging (each wave: its rows)
 
-  const int H = a.geo.H, DV = a.DV;
-  const int Pn = a.geo.N * H;
-  const int b = blockIdx.x;
-  const int jt = b / Pn, p = b - jt * Pn;
-  const int n = p / H, h = p - n * H;
-  const int dv0 = jt * DVT;
+  const int H = a.geo.H, DV = a.DV, CP = a.geo.cp, N = a.geo.N;
+  int p, jt;
+  if (!unit_of(blockIdx.x, N * CP * H, a.ntiles, p, jt)) return;
+  const int h = p % H, sg = (p / H) % CP, n = p / (H * CP);
+  if (MODE == 0 && sg == CP - 1) return;   // the last segment hands nothing on
+  const int col0 = jt * DVT;               // first column of the tile
+  const bool mtile = MODE == 0 && col0 < DK;   // transition columns: start at I, no input
+  const int dv0 = MODE == 0 ? (mtile ? 0 : col0 - DK) : col0;   // column of U (and o)
   int c0, nc, ts, tl;
-  seq_range(a.geo, n, c0, nc, ts, tl);
+  seg_range(a.geo, n, sg, c0, nc, ts, tl);
   const int w = wave_id();
   const int l = lane_id();
   const int dkw = w * (DK / 4);
@@ -382,6 +441,7 @@ __global__ __launch_bounds__(256) void k_scan_fwd(const ScanFwdArgs a) {
 
   f32x4 acc_h[MTH][NT];
   const int64_t sb = (int64_t)(n * H + h) * DK * DV;
+  const int64_t cpb = ((int64_t)sg * N * H + n * H + h) * DK;   // row 0 of this unit's CP tile
 #pragma unroll
   for (int mt = 0; mt < MTH; ++mt)
 #pragma unroll
@@ -390,21 +450,26 @@ __global__ __launch_bounds__(256) void k_scan_fwd(const ScanFwdArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int dk = dkw + 16 * mt + acc_row0() + i, dv = dv0 + 16 * nt + acc_col();
         float v = 0.f;
-        if (a.h0) v = (a.layout == 0) ? a.h0[sb + (int64_t)dk * DV + dv] : a.h0[sb + (int64_t)dv * DK + dk];
+        if (MODE == 0) v = (mtile && dk == col0 + 16 * nt + acc_col()) ? 1.f : 0.f;
+        else if (sg > 0) v = a.hstart[(cpb + dk) * DV + dv];
+        else if (a.h0) v = (a.layout == 0) ? a.h0[sb + (int64_t)dk * DV + dv] : a.h0[sb + (int64_t)dv * DK + dk];
         acc_h[mt][nt][i] = v;
       }
 #pragma unroll
   for (int mt = 0; mt < MTH; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) store_acc_t(sH, LDH, dkw + 16 * mt, 16 * nt, acc_h[mt][nt]);
+    for (int nt = 0; nt < NT; ++nt) store_acc_t2(sH, sHl, LDH, dkw + 16 * mt, 16 * nt, acc_h[mt][nt]);
 
   struct Ops {
-    frag wf[KS];           // W rows 16w
-    frag kf[MTH][KS64];    // Kt^T rows dkw.., k = chunk row
-    t4 u[NT];              // U (accumulator order, raw)
-    frag qf[KS];           // e^gamma Q rows 16w
-    frag pf[KS64];         // P rows 16w
-    float eL;              // e^{gamma_L}
+    frag wf[KS];            // W rows 16w
+    frag kf[MTH][KS64];     // K^T rows dkw.., k = chunk row
+    f32x4 u[NT];            // U (fp32, accumulator order, raw)
+    frag qf[KS];            // Q rows 16w
+    frag pf[KS64];          // P rows 16w, hi
+    frag pl[KS64];          // P rows 16w, lo
+    f32x4 eg;               // e^gamma of the lane's 4 rows
+    f32x4 ee;               // e^{gamma_L - gamma} of the lane's 4 rows
+    float eL;               // e^{gamma_L}
   };
   auto load_ops = [&](int c, Ops& o) {
     const int64_t ch = chb + c;
@@ -416,31 +481,39 @@ __global__ __launch_bounds__(256) void k_scan_fwd(const ScanFwdArgs a) {
     for (int mt = 0; mt < MTH; ++mt)
 #pragma unroll
       for (int ks = 0; ks < KS64; ++ks) o.kf[mt][ks] = frag_af<T, 64>(Kb, dkw / 16 + mt, ks);
-    const T* Ub = (const T*)a.Ua + ch * 64 * DV;
+    const float* Ub = a.Ua + ch * 64 * DV;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) o.u[nt] = *reinterpret_cast<const t4*>(Ub + acc_off(w, dv0 / 16 + nt, DV));
-    o.eL = a.gam[ch * GSTRIDE + 64 + 63];
+    for (int nt = 0; nt < NT; ++nt) o.u[nt] = *reinterpret_cast<const f32x4*>(Ub + acc_off(w, dv0 / 16 + nt, DV));
+    const float* gb = a.gam + ch * GSTRIDE;
+    o.ee = *reinterpret_cast<const f32x4*>(gb + 128 + rw + acc_row0());
+    o.eL = gb[64 + 63];
     if constexpr (OUT) {
-      const T* Qb = (const T*)a.Qgf + ch * 64 * DK;
+      const T* Qb = (const T*)a.Qf + ch * 64 * DK;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) o.qf[ks] = frag_af<T, DK>(Qb, w, ks);
       const T* Pb = (const T*)a.Pf + ch * 4096;
 #pragma unroll
       for (int ks = 0; ks < KS64; ++ks) o.pf[ks] = frag_af<T, 64>(Pb, w, ks);
+      if constexpr (SPLIT) {
+        const T* Pl = (const T*)a.Pfl + ch * 4096;
+#pragma unroll
+        for (int ks = 0; ks < KS64; ++ks) o.pl[ks] = frag_af<T, 64>(Pl, w, ks);
+      }
+      o.eg = *reinterpret_cast<const f32x4*>(gb + 64 + rw + acc_row0());
     }
   };
 
   auto process = [&](int c, Ops& o) {
     const int64_t ch = chb + c;
-    {
+    if constexpr (MODE != 0) {
       HS* hb = (HS*)a.hs + ch * DK * DV;
 #pragma unroll
       for (int mt = 0; mt < MTH; ++mt)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) store_acc4(hb + acc_off(dkw / 16 + mt, dv0 / 16 + nt, DV), acc_h[mt][nt]);
     }
-    __syncthreads();  // h^T in LDS is complete; last chunk's readers of Delta^T are done
-    // W h and (with OUT) Q h, rows 16w
+    __syncthreads();  // h^T in LDS is complete; last chunk's readers of Delta are done
+    // W h and (MODE 2) Q h, rows 16w
     f32x4 acc_d[NT], acc_o[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc_d[nt] = acc_o[nt] = zero4();
@@ -451,13 +524,22 @@ __global__ __launch_bounds__(256) void k_scan_fwd(const ScanFwdArgs a) {
         const frag bh = frag_rowk(sH, LDH, 16 * nt, ks * KW);
         acc_d[nt] = Mma<T>::mma(o.wf[ks], bh, acc_d[nt]);
         if constexpr (OUT) acc_o[nt] = Mma<T>::mma(o.qf[ks], bh, acc_o[nt]);
+        if constexpr (SPLIT) {
+          const frag bl = frag_rowk(sHl, LDH, 16 * nt, ks * KW);
+          acc_d[nt] = Mma<T>::mma(o.wf[ks], bl, acc_d[nt]);
+          if constexpr (OUT) acc_o[nt] = Mma<T>::mma(o.qf[ks], bl, acc_o[nt]);
+        }
       }
-    // Delta = U - W h
+    // Delta = U - W h; the output takes e^gamma (Q h)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc_d[nt][i] = to_f32(o.u[nt][i]) - acc_d[nt][i];
-      store_acc_t(sD, LDD, rw, 16 * nt, acc_d[nt]);
+      for (int i = 0; i < 4; ++i) acc_d[nt][i] = (mtile ? 0.f : o.u[nt][i]) - acc_d[nt][i];
+      store_acc_t2(sDE, sDEl, LDD, rw, 16 * nt, acc_d[nt] * o.ee);
+      if constexpr (OUT) {
+        store_acc_t2(sD, sDl, LDD, rw, 16 * nt, acc_d[nt]);
+        acc_o[nt] *= o.eg;
+      }
     }
     __syncthreads();  // Delta^T complete; all readers of h^T are done
 #pragma unroll
@@ -468,15 +550,28 @@ __global__ __launch_bounds__(256) void k_scan_fwd(const ScanFwdArgs a) {
     for (int ks = 0; ks < KS64; ++ks)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const frag bd = frag_rowk(sD, LDD, 16 * nt, ks * KW);
-        if constexpr (OUT) acc_o[nt] = Mma<T>::mma(o.pf[ks], bd, acc_o[nt]);
+        const frag be = frag_rowk(sDE, LDD, 16 * nt, ks * KW);
 #pragma unroll
-        for (int mt = 0; mt < MTH; ++mt) acc_h[mt][nt] = Mma<T>::mma(o.kf[mt][ks], bd, acc_h[mt][nt]);
+        for (int mt = 0; mt < MTH; ++mt) acc_h[mt][nt] = Mma<T>::mma(o.kf[mt][ks], be, acc_h[mt][nt]);
+        if constexpr (SPLIT) {
+          const frag bel = frag_rowk(sDEl, LDD, 16 * nt, ks * KW);
+#pragma unroll
+          for (int mt = 0; mt < MTH; ++mt) acc_h[mt][nt] = Mma<T>::mma(o.kf[mt][ks], bel, acc_h[mt][nt]);
+        }
+        if constexpr (OUT) {
+          const frag bd = frag_rowk(sD, LDD, 16 * nt, ks * KW);
+          acc_o[nt] = Mma<T>::mma(o.pf[ks], bd, acc_o[nt]);
+          if constexpr (SPLIT) {
+            const frag bdl = frag_rowk(sDl, LDD, 16 * nt, ks * KW);
+            acc_o[nt] = Mma<T>::mma(o.pf[ks], bdl, acc_o[nt]);
+            acc_o[nt] = Mma<T>::mma(o.pl[ks], bd, acc_o[nt]);
+          }
+        }
       }
 #pragma unroll
     for (int mt = 0; mt < MTH; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) store_acc_t(sH, LDH, dkw + 16 * mt, 16 * nt, acc_h[mt][nt]);
+      for (int nt = 0; nt < NT; ++nt) store_acc_t2(sH, sHl, LDH, dkw + 16 * mt, 16 * nt, acc_h[mt][nt]);
     if constexpr (OUT) {
       // each wave stages its 16 output rows in LDS and writes them back as
       // 16-byte pieces (LDS accesses of one wave are ordered: no barrier)
@@ -522,7 +617,17 @@ __global__ __launch_bounds__(256) void k_scan_fwd(const ScanFwdArgs a) {
     for (int s = 0; s < S - 1; ++s)
       if (cb + s < nc) process(cb + s, st[s]);
   }
-  if (a.hT) {
+  if (MODE == 0) {
+#pragma unroll
+    for (int mt = 0; mt < MTH; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int dk = dkw + 16 * mt + acc_row0() + i;
+          a.summ[(cpb + dk) * (DK + DV) + col0 + 16 * nt + acc_col()] = acc_h[mt][nt][i];
+        }
+  } else if (a.hT && sg == CP - 1) {
 #pragma unroll
     for (int mt = 0; mt < MTH; ++mt)
 #pragma unroll
@@ -537,15 +642,74 @@ __global__ __launch_bounds__(256) void k_scan_fwd(const ScanFwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// k_cp_chain: per (sequence, head, 64-column tile).  Serial over the CP
+// segments: X <- S X + Y with [S | Y] the segment summary (DK x (DK + 64)
+// slice, fp32), X the DK x 64 state slice held in LDS; fp32 FMA throughout.
+// Thread t owns column t % 64 and rows [(t / 64) DK/4, (t / 64 + 1) DK/4).
+template <int DK>
+__global__ __launch_bounds__(256) void k_cp_chain(const CpChainArgs a) {
+  constexpr int LDM = DK + 4;   // keeps float4 rows 16-byte aligned
+  constexpr int RPT = DK / 4;   // rows per thread
+  extern __shared__ __align__(16) char smem[];
+  float* sM = (float*)smem;          // S (r, m)
+  float* sX = sM + DK * LDM;         // X (m, j)
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  const int H = a.geo.H, N = a.geo.N, CP = a.geo.cp, DV = a.DV;
+  const int p = blockIdx.x, n = p / H, h = p - n * H;
+  const int dv0 = blockIdx.y * 64;
+  const int tid = threadIdx.x, j = tid & 63, r0 = (tid >> 6) * RPT;
+  const int64_t sb = (int64_t)(n * H + h) * DK * DV;
+  const int W = DK + DV;
+  for (int e = tid; e < DK * 64; e += 256) {
+    const int m = e >> 6, jj = e & 63;
+    float v = 0.f;
+    if (a.init) v = (a.layout == 0) ? a.init[sb + (int64_t)m * DV + dv0 + jj] : a.init[sb + (int64_t)(dv0 + jj) * DK + m];
+    sX[m * 64 + jj] = v;
+  }
+  for (int it = 0; it < CP - 1; ++it) {
+    const int s = a.bwd ? CP - 1 - it : it;        // segment whose summary is applied
+    const int so = a.bwd ? s - 1 : s + 1;          // segment whose state is produced
+    const float* Sb = a.summ + ((int64_t)s * N * H + n * H + h) * DK * W;
+    __syncthreads();  // previous X complete, previous readers of sM done
+    for (int e = tid; e < DK * DK / 4; e += 256) {
+      const int r = e / (DK / 4), c = (e - r * (DK / 4)) * 4;
+      *reinterpret_cast<f4*>(sM + r * LDM + c) = *reinterpret_cast<const f4*>(Sb + (int64_t)r * W + c);
+    }
+    float acc[RPT];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) acc[r] = Sb[(int64_t)(r0 + r) * W + DK + dv0 + j];
+    __syncthreads();
+    for (int m = 0; m < DK; m += 4) {
+      const float x0 = sX[m * 64 + j], x1 = sX[(m + 1) * 64 + j];
+      const float x2 = sX[(m + 2) * 64 + j], x3 = sX[(m + 3) * 64 + j];
+#pragma unroll
+      for (int r = 0; r < RPT; ++r) {
+        const f4 mv = *reinterpret_cast<const f4*>(sM + (r0 + r) * LDM + m);
+        acc[r] = fmaf(mv[0], x0, acc[r]);
+        acc[r] = fmaf(mv[1], x1, acc[r]);
+        acc[r] = fmaf(mv[2], x2, acc[r]);
+        acc[r] = fmaf(mv[3], x3, acc[r]);
+      }
+    }
+    __syncthreads();  // all reads of X done
+    float* ob = a.out + ((int64_t)so * N * H + n * H + h) * DK * DV;
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      sX[(r0 + r) * 64 + j] = acc[r];
+      ob[(int64_t)(r0 + r) * DV + dv0 + j] = acc[r];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host-side launchers
 
 template <typename T, int DK, bool BWD>
 static size_t wy_smem() {
   constexpr int P = pad_of<T>();
-  constexpr int LDK = DK + P, L64 = 64 + P, LDF = 68, DVB = dvb_of<T>(), LDV = DVB + P;
-  constexpr int R1 = cmax(cmax(2 * 64 * LDF * 4, (64 * LDK + 64 * LDV) * (int)sizeof(T)),
-                          (64 * LDK + 64 * L64) * (int)sizeof(T));
-  return 64 * LDK * sizeof(T) + R1 + 2 * 64 * L64 * sizeof(T) + 4 * 16 * 20 * 4 + 4 * 64 * 4;
+  constexpr int LDK = DK + P, LDF = 68, DVB = dvb_of<T>(), LDV = DVB + P;
+  constexpr int RA = cmax(64 * LDF * 4, 64 * LDK * (int)sizeof(T));
+  return 64 * LDK * sizeof(T) + RA + 64 * LDF * 4 + 64 * LDV * sizeof(T) + 4 * 16 * 20 * 4 + 4 * 64 * 4;
 }
 
 template <typename T, int DK, bool BWD>
@@ -572,29 +736,55 @@ hipError_t launch_wy(const WyArgs& a, bool f32, int DK, bool bwd, hipStream_t st
   return bwd ? launch_wy_t<bf16, 128, true>(a, st) : launch_wy_t<bf16, 128, false>(a, st);
 }
 
-template <typename T, typename HS, int DK, bool OUT>
-static hipError_t launch_scan_fwd_t(const ScanFwdArgs& a, int dvt, hipStream_t st) {
-  const int Pn = a.geo.N * a.geo.H;
-  const int grid = Pn * (a.DV / dvt);
-  if (grid == 0) return hipSuccess;
-  if (dvt == 16) hipLaunchKernelGGL((k_scan_fwd<T, HS, DK, 16, OUT>), dim3(grid), dim3(256), 0, st, a);
-  else if (dvt == 32) hipLaunchKernelGGL((k_scan_fwd<T, HS, DK, 32, OUT>), dim3(grid), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((k_scan_fwd<T, HS, DK, 64, OUT>), dim3(grid), dim3(256), 0, st, a);
+template <typename T, typename HS, int DK, int MODE>
+static hipError_t launch_scan_fwd_t(ScanFwdArgs a, int dvt, hipStream_t st) {
+  const int units = a.geo.N * a.geo.cp * a.geo.H;
+  a.ntiles = ((MODE == 0 ? DK : 0) + a.DV) / dvt;
+  const int grid = 8 * ((units + 7) / 8) * a.ntiles;
+  if (units == 0) return hipSuccess;
+  if (dvt == 16) hipLaunchKernelGGL((k_scan_fwd<T, HS, DK, 16, MODE>), dim3(grid), dim3(256), 0, st, a);
+  else if constexpr (sizeof(T) == 2) {
+    if (dvt == 32) hipLaunchKernelGGL((k_scan_fwd<T, HS, DK, 32, MODE>), dim3(grid), dim3(256), 0, st, a);
+    else if constexpr (DK == 64) hipLaunchKernelGGL((k_scan_fwd<T, HS, DK, 64, MODE>), dim3(grid), dim3(256), 0, st, a);
+    else return hipErrorInvalidValue;
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
-template <typename T, typename HS>
-static hipError_t launch_scan_fwd_d(const ScanFwdArgs& a, int DK, int dvt, hipStream_t st) {
-  const bool out = a.o != nullptr;
-  if (DK == 64) return out ? launch_scan_fwd_t<T, HS, 64, true>(a, dvt, st) : launch_scan_fwd_t<T, HS, 64, false>(a, dvt, st);
-  return out ? launch_scan_fwd_t<T, HS, 128, true>(a, dvt, st) : launch_scan_fwd_t<T, HS, 128, false>(a, dvt, st);
+template <typename T, typename HS, int DK>
+static hipError_t launch_scan_fwd_m(const ScanFwdArgs& a, int dvt, int mode, hipStream_t st) {
+  if (mode == 0) return launch_scan_fwd_t<T, float, DK, 0>(a, dvt, st);   // no snapshots: HS unused
+  if (mode == 1) return launch_scan_fwd_t<T, HS, DK, 1>(a, dvt, st);
+  return launch_scan_fwd_t<T, HS, DK, 2>(a, dvt, st);
 }
 
-hipError_t launch_scan_fwd(const ScanFwdArgs& a, bool f32, int hs_dtype, int DK, int dvt, hipStream_t st) {
-  if (f32) return launch_scan_fwd_d<float, float>(a, DK, dvt, st);
-  if (hs_dtype == GDR_F32) return launch_scan_fwd_d<bf16, float>(a, DK, dvt, st);
-  if (hs_dtype == GDR_F16) return launch_scan_fwd_d<bf16, f16>(a, DK, dvt, st);
-  return launch_scan_fwd_d<bf16, bf16>(a, DK, dvt, st);
+template <typename T, typename HS>
+static hipError_t launch_scan_fwd_d(const ScanFwdArgs& a, int DK, int dvt, int mode, hipStream_t st) {
+  if (DK == 64) return launch_scan_fwd_m<T, HS, 64>(a, dvt, mode, st);
+  return launch_scan_fwd_m<T, HS, 128>(a, dvt, mode, st);
+}
+
+hipError_t launch_scan_fwd(const ScanFwdArgs& a, bool f32, int hs_dtype, int DK, int dvt, int mode, hipStream_t st) {
+  if (f32) return launch_scan_fwd_d<float, float>(a, DK, dvt, mode, st);
+  if (hs_dtype == GDR_F32) return launch_scan_fwd_d<bf16, float>(a, DK, dvt, mode, st);
+  if (hs_dtype == GDR_F16) return launch_scan_fwd_d<bf16, f16>(a, DK, dvt, mode, st);
+  return launch_scan_fwd_d<bf16, bf16>(a, DK, dvt, mode, st);
+}
+
+template <int DK>
+static hipError_t launch_cp_chain_t(const CpChainArgs& a, hipStream_t st) {
+  const size_t sm = (size_t)(DK * (DK + 4) + DK * 64) * sizeof(float);
+  hipError_t e = hipFuncSetAttribute((const void*)k_cp_chain<DK>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_cp_chain<DK>, dim3(a.geo.N * a.geo.H, a.DV / 64), dim3(256), sm, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_cp_chain(const CpChainArgs& a, hipStream_t st) {
+  if (a.geo.N * a.geo.H == 0 || a.geo.cp <= 1) return hipSuccess;
+  return a.DK == 64 ? launch_cp_chain_t<64>(a, st) : launch_cp_chain_t<128>(a, st);
 }
 
 }  // namespace gdr

@@ -27,6 +27,10 @@ constexpr int cmax(int x, int y) { return x > y ? x : y; }
 // fragment is one contiguous 1 KB block) and per-tile results in
 // accumulator order (acc<R, C>), so every access of the serial scans is a
 // fully coalesced wave-wide load or store.
+// Operands are exact copies of the inputs wherever possible; where an
+// MFMA operand is a computed value whose bf16 rounding would dominate the
+// error (P, scale Q~^T), it is stored split (hi and lo).  Values the scans
+// add to their accumulators (U, scale P^T dO, scale Q~^T dO) are fp32.
 struct WyArgs {
   Geo geo;
   int DV;
@@ -39,49 +43,73 @@ struct WyArgs {
   const float* g;
   float* gam;   // [GSTRIDE]: gamma, e^gamma, e^{gamma_L - gamma}
   void* Wf;     // afrag<64, DK>: W (rows r, k = dk)
-  void* KtTf;   // afrag<DK, 64>: (E K)^T, E = e^{gamma_L - gamma} (nullable)
-  void* Ua;     // acc<64, DV>: U
-  void* Qgf;    // afrag<64, DK>: e^gamma Q                    (forward)
-  void* Pf;     // afrag<64, 64>: P = Q K^T * Gam (rows r)     (forward)
-  float* Tm;    // [64][64] fp32 row-major: T                 (backward)
-  void* WTf;    // afrag<DK, 64>: W^T                          (backward)
-  void* PsTf;   // afrag<64, 64>: scale P^T (rows s)           (backward)
-  void* QgsTf;  // afrag<DK, 64>: scale (e^gamma Q)^T          (backward)
-  void* Ktf;    // afrag<64, DK>: E K                          (backward)
-  void* dOf;    // afrag<DV, 64>: dO^T                         (backward)
+  float* Ua;    // acc<64, DV> fp32: U
+  void* KtTf;   // afrag<DK, 64>: K^T (exact; nullable)
+  void* Qf;     // afrag<64, DK>: Q (exact)                          (forward)
+  void* Pf;     // afrag<64, 64>: P = Q K^T * Gam (rows r), hi part  (forward)
+  void* Pfl;    // the lo part (bf16 only)                           (forward)
+  float* Tm;    // [64][64] fp32 row-major: T                       (backward)
+  void* WTf;    // afrag<DK, 64>: W^T                                (backward)
+  void* Kf;     // afrag<64, DK>: K (exact)                          (backward)
+  float* dDl;   // acc<64, DV> fp32: scale P^T dO                    (backward)
+  float* Z;     // acc<DK, DV> fp32: scale (e^gamma Q)^T dO          (backward)
 };
 
+// The serial scans run one workgroup per (unit, column tile); a unit is a
+// (sequence, CP segment, head).  In the CP summary mode (MODE 0) the columns
+// are those of the augmented state [transition | state from zero], DK + DV
+// wide; otherwise the DV columns of the state.
 struct ScanFwdArgs {
   Geo geo;
   int DV;
+  int ntiles;        // column tiles per unit (set by the launcher)
   int layout;        // 0: KV, 1: VK for h0 / hT
   float scale;
   const float* h0;   // nullable
   float* hT;         // nullable
+  const float* hstart;  // CP: [cp][N][H][DK][DV] fp32 start state of each segment (s >= 1)
+  float* summ;          // CP summary out: [cp][N][H][DK][DK + DV] fp32 (s < cp - 1)
   const float* gam;
   const void* Wf;
   const void* KtTf;
-  const void* Ua;
-  const void* Qgf;   // output operands (o == nullptr: no output)
+  const float* Ua;
+  const void* Qf;    // output operands (MODE 2)
   const void* Pf;
+  const void* Pfl;
   void* o;
-  void* hs;          // acc<DK, DV> per chunk-head: state at chunk start (required)
+  void* hs;          // acc<DK, DV> per chunk-head: state at chunk start (MODE 1, 2)
 };
 
 struct ScanBwdArgs {
   Geo geo;
   int DV;
+  int ntiles;
   int layout;
   const float* dhT;  // nullable
   float* dh0;        // nullable
+  const float* dhend;   // CP: [cp][N][H][DK][DV] fp32 gradient at each segment's end (s < cp - 1)
+  float* summ;          // CP summary out: [cp][N][H][DK][DK + DV] fp32 (s >= 1)
   const float* gam;
-  const void* Ktf;
-  const void* PsTf;
-  const void* QgsTf;
+  const void* Kf;
   const void* WTf;
-  const void* dOf;
-  void* dhs;         // acc<DK, DV>: gradient of the state at chunk end
-  void* dD;          // acc<64, DV>: gradient of Delta
+  const float* dDl;
+  const float* Z;
+  void* dhs;         // acc<DK, DV> (io dtype): gradient of the state at chunk end
+  float* dD;         // acc<64, DV> fp32: gradient of Delta
+};
+
+// Hand-off of the CP segment states, per (sequence, head, 64-column tile):
+// forward, h_start[s + 1] = M_s h_start[s] + b_s from h_start[0] = h0;
+// backward, dh_end[s - 1] = X_s dh_end[s] + d_s from dh_end[cp - 1] = dh_T,
+// with [M_s | b_s] / [X_s | d_s] the segment summaries.
+struct CpChainArgs {
+  Geo geo;             // N, H, cp
+  int DK, DV;
+  int layout;          // of init
+  int bwd;
+  const float* init;   // h0 (forward) / dh_T (backward), user layout; nullable (zeros)
+  const float* summ;   // [cp][N][H][DK][DK + DV]
+  float* out;          // [cp][N][H][DK][DV]: h_start (forward) / dh_end (backward)
 };
 
 struct GradArgs {
@@ -95,11 +123,11 @@ struct GradArgs {
   const float* beta;
   const float* gam;
   const void* Wf;
-  const void* Ua;
+  const float* Ua;
   const float* Tm;
   const void* hs;
   const void* dhs;
-  const void* dD;
+  const float* dD;
   void* dq;
   void* dk;
   void* dv;
@@ -163,8 +191,9 @@ __device__ __forceinline__ void store8(T* dst, const float* v) {
 // Write rows [0, RB) of an afrag<*, K> matrix (dst already points at the
 // first fragment of row tile i0 / 16) with element (i, k) = f(i, k).  Each
 // thread writes 16-byte pieces; consecutive threads write consecutive pieces.
+// With dlo (16-bit T only) the values are split: hi into dst, lo into dlo.
 template <typename T, int RB, int K, typename F>
-__device__ __forceinline__ void write_afrag(T* dst, F&& f) {
+__device__ __forceinline__ void write_afrag(T* dst, F&& f, T* dlo = nullptr) {
   constexpr int KW = Mma<T>::KW, KPL = Mma<T>::KPL;
   constexpr int PE = 16 / sizeof(T);                // elements per piece
   constexpr int NPIECE = RB * K / PE;
@@ -180,10 +209,16 @@ __device__ __forceinline__ void write_afrag(T* dst, F&& f) {
     }
     if constexpr (PE == 8) {
       typedef T t8 __attribute__((ext_vector_type(8)));
-      t8 w;
+      t8 w, wl;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) w[j] = from_f32<T>(v[j]);
+      for (int j = 0; j < 8; ++j) {
+        T h, lo;
+        split2<T>(v[j], h, lo);
+        w[j] = h;
+        wl[j] = lo;
+      }
       *reinterpret_cast<t8*>(dst + (int64_t)p * PE) = w;
+      if (dlo) *reinterpret_cast<t8*>(dlo + (int64_t)p * PE) = wl;
     } else {
       *reinterpret_cast<f32x4*>(dst + (int64_t)p * PE) = (f32x4){v[0], v[1], v[2], v[3]};
     }
@@ -205,8 +240,11 @@ __device__ __forceinline__ f32x4 load4f(const T* p) {
 hipError_t launch_plan(const int* cu, int N, int T_total, int nchunks, int* seq_chunk, int* chunk_seq,
                        hipStream_t st);
 hipError_t launch_wy(const WyArgs& a, bool f32, int DK, bool bwd, hipStream_t st);
-hipError_t launch_scan_fwd(const ScanFwdArgs& a, bool f32, int hs_dtype, int DK, int dvt, hipStream_t st);
-hipError_t launch_scan_bwd(const ScanBwdArgs& a, bool f32, int DK, int dvt, hipStream_t st);
+// mode 0: CP segment summaries; forward 1: snapshots only, 2: snapshots and
+// output; backward 1: the reverse scan proper
+hipError_t launch_scan_fwd(const ScanFwdArgs& a, bool f32, int hs_dtype, int DK, int dvt, int mode, hipStream_t st);
+hipError_t launch_scan_bwd(const ScanBwdArgs& a, bool f32, int DK, int dvt, int mode, hipStream_t st);
+hipError_t launch_cp_chain(const CpChainArgs& a, hipStream_t st);
 hipError_t launch_grad(const GradArgs& a, bool f32, int hs_dtype, int DK, hipStream_t st);
 
 }  // namespace gdr

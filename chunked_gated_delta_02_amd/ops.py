@@ -6,8 +6,10 @@ in libgdr's HIP kernels (loaded through ``_lib``; missing library = error).
 The features follow FlashQLA PR #34 ("SM120/121 : Add support for fused
 backward kernel", section "Current status"): fixed-length and packed
 variable-length inputs, KV/VK state layouts, initial and final states,
-autograd.  ``h_store`` selects the dtype of the per-chunk state snapshots
-(the fp16 ``h_dtype`` of the PR's draft page is ``h_store="f16"``).
+autograd, intra-card context parallelism (``cp_segments``, which the
+forward and the backward may set differently).  ``h_store`` selects the dtype
+of the per-chunk state snapshots (the fp16 ``h_dtype`` of the PR's draft page
+is ``h_store="f16"``).
 """
 from __future__ import annotations
 
@@ -75,10 +77,10 @@ def _state_shape(N, H, DK, DV, layout):
 
 
 def chunk_gdr_fwd(q, k, v, beta, g, cu_seqlens=None, h0=None, layout="KV", scale=None,
-                  output_final_state=True, save_states=False, h_store="f32"):
+                  output_final_state=True, save_states=False, h_store="f32", cp_segments=1):
     """Forward.  Returns (o, h_T or None, h_saved or None)."""
     _check_tensors(q, k, v, beta, g, cu_seqlens, [("h0", h0)])
-    p = make_problem(q, v, cu_seqlens, layout, scale, h_store)
+    p = make_problem(q, v, cu_seqlens, layout, scale, h_store, cp_segments)
     B, T, H, DK = q.shape
     DV = v.shape[-1]
     N = p.num_seqs
@@ -104,12 +106,12 @@ def chunk_gdr_fwd(q, k, v, beta, g, cu_seqlens=None, h0=None, layout="KV", scale
 
 
 def chunk_gdr_bwd(q, k, v, beta, g, do, cu_seqlens=None, h0=None, dhT=None, h_saved=None,
-                  layout="KV", scale=None, h_store="f32", need_dh0=True):
+                  layout="KV", scale=None, h_store="f32", need_dh0=True, cp_segments=1):
     """Backward.  Returns dict(dq, dk, dv, dbeta, dg, dh0)."""
     _check_tensors(q, k, v, beta, g, cu_seqlens, [("h0", h0), ("do", do), ("dhT", dhT), ("h_saved", h_saved)])
     if do.shape != v.shape or do.dtype != v.dtype:
         raise ValueError("do must match v in shape and dtype")
-    p = make_problem(q, v, cu_seqlens, layout, scale, h_store)
+    p = make_problem(q, v, cu_seqlens, layout, scale, h_store, cp_segments)
     B, T, H, DK = q.shape
     DV = v.shape[-1]
     N = p.num_seqs
@@ -141,12 +143,13 @@ class ChunkGDRFunction(torch.autograd.Function):
     so the backward skips the state recomputation."""
 
     @staticmethod
-    def forward(ctx, q, k, v, beta, g, h0, cu_seqlens, layout, scale, h_store, output_final_state):
+    def forward(ctx, q, k, v, beta, g, h0, cu_seqlens, layout, scale, h_store, output_final_state,
+                cp_fwd, cp_bwd):
         o, hT, h_saved = chunk_gdr_fwd(q, k, v, beta, g, cu_seqlens=cu_seqlens, h0=h0, layout=layout,
                                        scale=scale, output_final_state=output_final_state,
-                                       save_states=True, h_store=h_store)
+                                       save_states=True, h_store=h_store, cp_segments=cp_fwd)
         ctx.save_for_backward(q, k, v, beta, g, h0, cu_seqlens, h_saved)
-        ctx.layout, ctx.scale, ctx.h_store = layout, scale, h_store
+        ctx.layout, ctx.scale, ctx.h_store, ctx.cp_bwd = layout, scale, h_store, cp_bwd
         ctx.has_h0 = h0 is not None
         if hT is None:
             return o
@@ -158,12 +161,15 @@ class ChunkGDRFunction(torch.autograd.Function):
         r = chunk_gdr_bwd(q, k, v, beta, g, do.contiguous(), cu_seqlens=cu_seqlens, h0=h0,
                           dhT=None if dhT is None else dhT.contiguous(), h_saved=h_saved,
                           layout=ctx.layout, scale=ctx.scale, h_store=ctx.h_store,
-                          need_dh0=ctx.has_h0 and ctx.needs_input_grad[5])
-        return (r["dq"], r["dk"], r["dv"], r["dbeta"], r["dg"], r["dh0"], None, None, None, None, None)
+                          need_dh0=ctx.has_h0 and ctx.needs_input_grad[5], cp_segments=ctx.cp_bwd)
+        return (r["dq"], r["dk"], r["dv"], r["dbeta"], r["dg"], r["dh0"]) + (None,) * 7
 
 
 def chunk_gdr(q, k, v, beta, g, h0=None, cu_seqlens=None, layout="KV", scale=None,
-              output_final_state=True, h_store="f32"):
-    """Chunked gated delta rule with autograd.  Returns o, or (o, h_T)."""
+              output_final_state=True, h_store="f32", cp_segments=1, cp_segments_bwd=None):
+    """Chunked gated delta rule with autograd.  Returns o, or (o, h_T).
+    ``cp_segments_bwd`` (default: ``cp_segments``) sets the backward's
+    intra-card context parallelism independently of the forward's."""
+    cp_bwd = cp_segments if cp_segments_bwd is None else cp_segments_bwd
     return ChunkGDRFunction.apply(q, k, v, beta, g, h0, cu_seqlens, layout, scale, h_store,
-                                  output_final_state)
+                                  output_final_state, cp_segments, cp_bwd)

@@ -78,9 +78,24 @@ typedef struct {
   int32_t h_store_dtype; /* per-chunk state snapshots: GDR_F32, GDR_F16 or GDR_BF16
                             (GDR_F32 only when io_dtype is GDR_F32)                 */
   int32_t layout;        /* GDR_LAYOUT_KV or GDR_LAYOUT_VK for h0,hT,dhT,dh0       */
-  int32_t cp_segments;   /* intra-card context-parallel segments (>= 1)            */
+  int32_t cp_segments;   /* intra-card context parallelism: each sequence is cut
+                            into this many chunk-aligned segments whose state
+                            scans run concurrently (1 = off, at most 1024);
+                            see below                                               */
   float scale;           /* <= 0 selects dk^-1/2                                    */
 } gdr_problem;
+
+/* Intra-card context parallelism (the "intra-card CP" of FlashQLA PR #34,
+ * "Current status").  The state recursion of a chunk is affine in the state,
+ * h' = M_c h + b_c with M_c = e^{gamma_L} I - Kt^T W, so a sequence cut into
+ * segments is scanned in three steps: every segment but the last computes its
+ * transition [prod M_c | state from zero] by scanning the augmented state
+ * [I | 0] (the identity columns take no input); a short serial pass hands
+ * the start state from segment to segment in fp32; then every segment runs
+ * the ordinary scan from its start state.  The backward mirrors this on dh
+ * with the transposed transitions.  Results equal cp_segments = 1 up to
+ * rounding; the forward and the backward of one problem may use different
+ * cp_segments (the saved snapshots do not depend on it). */
 
 /* Validate a problem description.  Reads no tensor contents. */
 gdr_status gdr_check(const gdr_problem* p);
@@ -122,7 +137,11 @@ enum {
   GDR_KERNEL_SCAN_FWD = 2,   /* state scan with fused output (bwd: recompute only) */
   GDR_KERNEL_SCAN_BWD = 3,   /* reverse dh scan                                    */
   GDR_KERNEL_GRAD = 4,       /* fused chunk-parallel gradient kernel               */
-  GDR_NUM_KERNELS = 5
+  GDR_KERNEL_CP_SCAN_FWD = 5,  /* cp_segments > 1: segment transitions (forward)    */
+  GDR_KERNEL_CP_CHAIN_FWD = 6, /* cp_segments > 1: start-state hand-off (forward)   */
+  GDR_KERNEL_CP_SCAN_BWD = 7,  /* cp_segments > 1: segment transitions (backward)   */
+  GDR_KERNEL_CP_CHAIN_BWD = 8, /* cp_segments > 1: dh hand-off (backward)           */
+  GDR_NUM_KERNELS = 9
 };
 /* events: NULL to switch timing off for the calling thread, else an array of
  * 2 * GDR_NUM_KERNELS hipEvent_t handles (start, stop per kernel id; NULL

@@ -33,21 +33,25 @@ def to64(t):
     return None if t is None else t.detach().to("cpu").double().numpy()
 
 
-def run_gpu(w: gin.Workload, inp: dict, h_store=None, saved=True, device="cuda"):
-    """libgdr forward + backward; returns dict of fp64 NumPy arrays."""
+def run_gpu(w: gin.Workload, inp: dict, h_store=None, saved=True, device="cuda", cp_fwd=None, cp_bwd=None):
+    """libgdr forward + backward; returns dict of fp64 NumPy arrays.  The
+    context-parallel segment counts default to the workload's."""
     dev = {k: (v.to(device) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
     hs = h_store or w.h_store
-    say("[gpu] %s fwd: B=%d T=%d H=%d DK=%d DV=%d io=%s layout=%s h0=%s varlen=%s h_store=%s" % (
+    cp_fwd = w.cp_segments if cp_fwd is None else cp_fwd
+    cp_bwd = w.cp_segments if cp_bwd is None else cp_bwd
+    say("[gpu] %s fwd: B=%d T=%d H=%d DK=%d DV=%d io=%s layout=%s h0=%s varlen=%s h_store=%s cp=%d/%d" % (
         w.name, dev["q"].shape[0], dev["q"].shape[1], w.H, w.DK, w.DV, w.io_dtype, w.layout,
-        inp["h0"] is not None, inp["cu_seqlens"] is not None, hs))
+        inp["h0"] is not None, inp["cu_seqlens"] is not None, hs, cp_fwd, cp_bwd))
     o, hT, h_saved = ops.chunk_gdr_fwd(dev["q"], dev["k"], dev["v"], dev["beta"], dev["g"],
                                        cu_seqlens=dev["cu_seqlens"], h0=dev["h0"], layout=w.layout,
-                                       output_final_state=True, save_states=saved, h_store=hs)
+                                       output_final_state=True, save_states=saved, h_store=hs,
+                                       cp_segments=cp_fwd)
     torch.cuda.synchronize()
     say("[gpu] %s bwd (saved states: %s)" % (w.name, saved))
     r = ops.chunk_gdr_bwd(dev["q"], dev["k"], dev["v"], dev["beta"], dev["g"], dev["do"],
                           cu_seqlens=dev["cu_seqlens"], h0=dev["h0"], dhT=dev["dhT"],
-                          h_saved=h_saved, layout=w.layout, h_store=hs)
+                          h_saved=h_saved, layout=w.layout, h_store=hs, cp_segments=cp_bwd)
     torch.cuda.synchronize()
     out = dict(o=to64(o), hT=to64(hT))
     out.update({k: to64(v) for k, v in r.items()})

@@ -124,10 +124,18 @@ def test_fwd_cu_seqlens_consistency(lib):
     assert call_fwd(pv, fwd_args(pv)) == _lib.GDR_ERR_INVALID_ARG
 
 
-def test_fwd_unsupported_context_parallel_reports(lib):
-    p = good(cp_segments=4)
-    st = _lib.gdr_check(p)
-    assert st in (_lib.GDR_OK, _lib.GDR_ERR_UNSUPPORTED)
+def test_context_parallel_limits_and_workspace(lib):
+    assert _lib.gdr_check(good(cp_segments=4)) == _lib.GDR_OK
+    assert _lib.gdr_check(good(cp_segments=1024)) == _lib.GDR_OK
+    assert _lib.gdr_check(good(cp_segments=1025)) == _lib.GDR_ERR_UNSUPPORTED
+    # CP needs the segment summaries [DK x (DK + DV)] and hand-off states
+    # [DK x DV] (fp32) per (segment, sequence, head) on top of the plain plan
+    p1, p4 = good(), good(cp_segments=4)
+    extra = 4 * p4.num_seqs * p4.heads * p4.dk * (2 * p4.dv + p4.dk) * 4
+    for f in (lambda p: _lib.gdr_fwd_workspace_bytes(p), lambda p: _lib.gdr_bwd_workspace_bytes(p, True)):
+        assert extra <= f(p4) - f(p1) <= extra + 512
+    # the saved snapshots do not depend on the segmentation
+    assert _lib.gdr_h_saved_bytes(p1) == _lib.gdr_h_saved_bytes(p4)
 
 
 def test_bwd_validation(lib):

@@ -20,9 +20,9 @@ SMALL = {
     "cfg1_fixed_bf16_ragged": C[1].replace(name="cfg1_small", B=2, T=333, H=3),
     "cfg2_varlen_bf16": C[2].replace(name="cfg2_small", H=4, lengths=[70, 0, 1, 200, 129, 64],
                                      len_range=None),
-    "cfg3_slowdecay_f32state": C[3].replace(name="cfg3_small", T=1000, H=2, cp_segments=1),
-    "cfg3_slowdecay_f16state": C[3].replace(name="cfg3_small_f16", T=1000, H=2, cp_segments=1,
-                                            h_store="f16"),
+    "cfg3_slowdecay_f32state_nocp": C[3].replace(name="cfg3_small", T=1000, H=2, cp_segments=1),
+    "cfg3_slowdecay_f16state_nocp": C[3].replace(name="cfg3_small_f16", T=1000, H=2, cp_segments=1,
+                                                 h_store="f16"),
     "cfg4_widev_bf16": C[4].replace(name="cfg4_small", B=2, T=200, H=2),
     "fp32_dk128": C[0].replace(name="fp32_dk128", B=2, T=150, H=2, DK=128, DV=128, layout="KV"),
     "fp32_dv192_varlen": C[0].replace(name="fp32_dv192_varlen", H=2, DK=64, DV=192,
@@ -166,6 +166,65 @@ def test_autograd_matches_explicit_backward():
 
 
 # ---------------------------------------------------------------------------
+# intra-card context parallelism: every case against the oracle (the
+# segmented scan must reach the un-segmented result within the tolerance)
+
+CP = {
+    # slow decay, 16 chunks in 8 segments of 2
+    "cp8_slowdecay": C[3].replace(name="cp8_slowdecay", T=1000, H=2),
+    "cp8_slowdecay_f16state": C[3].replace(name="cp8_slowdecay_f16", T=1000, H=2, h_store="f16"),
+    # packed batch with empty and one-token sequences, VK, initial states
+    "cp3_varlen_vk_h0": C[2].replace(name="cp3_varlen", H=2, lengths=[70, 0, 1, 200, 129, 300],
+                                     len_range=None, cp_segments=3),
+    # fp32 path; 5 chunks in segments of 2, 2, 1 and an empty last segment
+    "cp4_fp32_empty_last_segment": C[0].replace(name="cp4_fp32", T=300, cp_segments=4),
+    # almost no decay: the segment transitions are far from zero
+    "cp5_nodecay_h0": C[1].replace(name="cp5_nodecay", B=2, T=640, H=2, g_mean=6.0, has_h0=True,
+                                   cp_segments=5),
+    # more segments than chunks
+    "cp7_short": C[1].replace(name="cp7_short", B=1, T=100, H=2, has_h0=True, cp_segments=7),
+    "cp3_dk64_dv192": C[1].replace(name="cp3_dk64_dv192", B=1, T=400, H=2, DK=64, DV=192, has_h0=True,
+                                   cp_segments=3),
+}
+
+
+@pytest.mark.parametrize("case", sorted(CP))
+def test_context_parallel_parity(case):
+    w = CP[case]
+    say("[case] %s" % case)
+    inp = gin.generate(w)
+    got = run_gpu(w, inp)
+    ref = run_oracle(w, inp)
+    compare(w, got, ref)
+
+
+def test_context_parallel_mixed_forward_backward_settings():
+    w = CP["cp5_nodecay_h0"]
+    say("[case] mixed CP settings %s" % w.name)
+    inp = gin.generate(w)
+    ref = run_oracle(w, inp)
+    for cf, cb, saved in ((5, 1, True), (1, 5, True), (3, 5, True), (5, 5, False)):
+        say("[case] cp fwd %d bwd %d saved %s" % (cf, cb, saved))
+        compare(w, run_gpu(w, inp, cp_fwd=cf, cp_bwd=cb, saved=saved), ref)
+
+
+def test_context_parallel_autograd():
+    w = CP["cp7_short"]
+    say("[case] CP autograd")
+    inp = gin.generate(w)
+    dev = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    leaves = {n: dev[n].clone().requires_grad_(True) for n in ("q", "k", "v", "beta", "g", "h0")}
+    o, hT = ops.chunk_gdr(leaves["q"], leaves["k"], leaves["v"], leaves["beta"], leaves["g"],
+                          h0=leaves["h0"], layout=w.layout, cp_segments=7, cp_segments_bwd=2)
+    torch.autograd.backward([o, hT], [dev["do"], dev["dhT"]])
+    torch.cuda.synchronize()
+    got = dict(o=to64(o.detach()), hT=to64(hT.detach()))
+    got.update({g: to64(leaves[n].grad) for n, g in (("q", "dq"), ("k", "dk"), ("v", "dv"),
+                                                      ("beta", "dbeta"), ("g", "dg"), ("h0", "dh0"))})
+    compare(w, got, run_oracle(w, inp))
+
+
+# ---------------------------------------------------------------------------
 # full sizes of the workloads, the launch configuration the benchmark times,
 # checked on sampled heads (each head is an independent problem)
 
@@ -184,3 +243,14 @@ def test_parity_full_size_sampled_heads(name):
     got = run_gpu(w, inp)
     ref = run_oracle(w, inp, heads=heads)
     compare(w, got, ref, heads=heads)
+
+
+def test_parity_full_size_long_context_cp8_both_snapshot_dtypes():
+    # T = 65536 in 8 context-parallel segments; fp32 and fp16 snapshots
+    w, heads = C[3], [6]
+    say("[case] full-size %s heads %s" % (w.name, heads))
+    inp = gin.generate(w)
+    ref = run_oracle(w, inp, heads=heads)
+    for hs in ("f32", "f16"):
+        say("[case] h_store %s" % hs)
+        compare(w, run_gpu(w, inp, h_store=hs), ref, heads=heads)
