@@ -44,6 +44,12 @@ def parse():
                     help="snapshot dtype (default: the workload's)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the oracle sample")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="after the timed region, run one elementwise copy kernel of this many MiB "
+                         "(fp32, read once + written once) as the scale reference of --pmc byte counters")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
+                    help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, then "
+                         "WRITE_SIZE) of a run with --calibrate-copy-mib into profiles/<kernel>_<workload>_pmc.json")
     return ap.parse_args()
 
 
@@ -186,6 +192,46 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+def ingest_pmc(fetch_csv, write_csv, workload, copy_mib, dispatches_per_step):
+    """Per-launch HBM bytes of k_grad from two rocprofv3 --pmc runs, scaled by
+    what the same counters read for the calibration copy kernel."""
+    import csv
+    import statistics
+
+    def per_kernel(path, counter):
+        vals = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+    copy_f = [v for k, v in fetch.items() if "MulFunctor" in k]
+    copy_w = [v for k, v in write.items() if "MulFunctor" in k]
+    if not copy_f or not copy_w:
+        raise SystemExit("calibration copy kernel not found in the counter files")
+    ref_kib = copy_mib * 1024.0
+    f_scale = ref_kib / statistics.median(copy_f[0])
+    w_scale = ref_kib / statistics.median(copy_w[0])
+    name = [k for k in fetch if "k_grad" in k]
+    if not name:
+        raise SystemExit("k_grad not found in the counter files")
+    kf = statistics.median(fetch[name[0]]) * f_scale * 1024.0
+    kw = statistics.median(write[[k for k in write if "k_grad" in k][0]]) * w_scale * 1024.0
+    out = {"kernel": "k_grad", "workload": workload, "source_hash": kernel_source_hash(),
+           "fetch_bytes_per_launch": kf, "write_bytes_per_launch": kw,
+           "hbm_bytes_per_launch": kf + kw,
+           "calibration": {"copy_mib": copy_mib, "fetch_scale": f_scale, "write_scale": w_scale},
+           "files": [os.path.basename(fetch_csv), os.path.basename(write_csv)]}
+    path = os.path.join(ROOT, "profiles", "grad_bwd_%s_pmc.json" % workload)
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
 def measured_traffic(kernel, workload):
     """HBM bytes per launch from committed rocprofv3 --pmc summaries, if they
     were taken on the current kernel sources; else None."""
@@ -240,6 +286,11 @@ def cpu_baseline(w, inp, target_s):
 
 def main():
     args = parse()
+    if args.ingest_pmc:
+        from chunked_gated_delta_02_amd import inputs as gin
+        ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], gin.CONFIGS[args.config].name,
+                   args.calibrate_copy_mib or 256, 1)
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(asked for --gpus %d)" % args.gpus, file=sys.stderr)
@@ -310,6 +361,14 @@ def main():
     t_host1 = time.perf_counter()
     total_ms = hip.elapsed_ms(e0, e1)
     ms_step = total_ms / args.steps
+    if args.calibrate_copy_mib:
+        # scale reference for --pmc byte counters: fp32 elementwise multiply by
+        # one, reading and writing calibrate_copy_mib MiB once each
+        src = torch.ones(args.calibrate_copy_mib * (1 << 18), dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     # per-kernel averages
     per = {}

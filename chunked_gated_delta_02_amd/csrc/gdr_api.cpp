@@ -146,13 +146,14 @@ gdr::Geo make_geo(const gdr_problem* p, const Plan& pl, const int32_t* cu, char*
 
 // Column tile of the serial scans.  A wider tile reads each chunk operand
 // once for more columns, a narrower one gives more workgroups: take the
-// widest that still gives two workgroups per compute unit (512 in all), among
-// the tiles that fit in registers without spilling (64 only with DK = 64).
-// The fp32 path always uses 16 (its operand fragments are 8x larger per k).
+// widest that still gives one workgroup per compute unit (256 in all; the
+// scans run one or two per CU), among the tiles that fit in registers
+// without spilling (64 only with DK = 64).  The fp32 path always uses 16
+// (its operand fragments are 8x larger per k).
 int pick_dvt(long units, int cols, bool f32, int dk) {
   if (f32) return 16;
-  if (dk == 64 && units * (cols / 64) >= 512) return 64;
-  if (units * (cols / 32) >= 512) return 32;
+  if (dk == 64 && units * (cols / 64) >= 256) return 64;
+  if (units * (cols / 32) >= 256) return 32;
   return 16;
 }
 

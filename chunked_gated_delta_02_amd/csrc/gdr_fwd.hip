@@ -642,60 +642,81 @@ __global__ __launch_bounds__(256) void k_scan_fwd(const ScanFwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// k_cp_chain: per (sequence, head, 64-column tile).  Serial over the CP
-// segments: X <- S X + Y with [S | Y] the segment summary (DK x (DK + 64)
-// slice, fp32), X the DK x 64 state slice held in LDS; fp32 FMA throughout.
-// Thread t owns column t % 64 and rows [(t / 64) DK/4, (t / 64 + 1) DK/4).
+// k_cp_chain: per (sequence, head, 16-column tile).  Serial over the CP
+// segments: X <- S X + Y with [S | Y] the segment summary (DK x (DK + 16)
+// slice, fp32) and X the DK x 16 state slice in LDS; fp32 FMA throughout.
+// Thread t owns column t % 16 and rows [(t / 16) DK/16, (t / 16 + 1) DK/16).
+// The next segment's S is loaded into registers while the current hop
+// computes, and stored to the other LDS buffer after it.
 template <int DK>
 __global__ __launch_bounds__(256) void k_cp_chain(const CpChainArgs a) {
   constexpr int LDM = DK + 4;   // keeps float4 rows 16-byte aligned
-  constexpr int RPT = DK / 4;   // rows per thread
+  constexpr int RPT = DK / 16;  // rows per thread
+  constexpr int NPF = DK * DK / 4 / 256;   // float4 pieces of S per thread
   extern __shared__ __align__(16) char smem[];
-  float* sM = (float*)smem;          // S (r, m)
-  float* sX = sM + DK * LDM;         // X (m, j)
+  float* sM = (float*)smem;          // two buffers of S (r, m)
+  float* sX = sM + 2 * DK * LDM;     // X (m, j)
   typedef float f4 __attribute__((ext_vector_type(4)));
   const int H = a.geo.H, N = a.geo.N, CP = a.geo.cp, DV = a.DV;
   const int p = blockIdx.x, n = p / H, h = p - n * H;
-  const int dv0 = blockIdx.y * 64;
-  const int tid = threadIdx.x, j = tid & 63, r0 = (tid >> 6) * RPT;
+  const int dv0 = blockIdx.y * 16;
+  const int tid = threadIdx.x, j = tid & 15, r0 = (tid >> 4) * RPT;
   const int64_t sb = (int64_t)(n * H + h) * DK * DV;
   const int W = DK + DV;
-  for (int e = tid; e < DK * 64; e += 256) {
-    const int m = e >> 6, jj = e & 63;
+  auto seg_of = [&](int it) { return a.bwd ? CP - 1 - it : it; };   // summary applied at hop it
+  auto summ = [&](int s) { return a.summ + ((int64_t)s * N * H + n * H + h) * DK * W; };
+  for (int e = tid; e < DK * 16; e += 256) {
+    const int m = e >> 4, jj = e & 15;
     float v = 0.f;
     if (a.init) v = (a.layout == 0) ? a.init[sb + (int64_t)m * DV + dv0 + jj] : a.init[sb + (int64_t)(dv0 + jj) * DK + m];
-    sX[m * 64 + jj] = v;
+    sX[m * 16 + jj] = v;
   }
-  for (int it = 0; it < CP - 1; ++it) {
-    const int s = a.bwd ? CP - 1 - it : it;        // segment whose summary is applied
-    const int so = a.bwd ? s - 1 : s + 1;          // segment whose state is produced
-    const float* Sb = a.summ + ((int64_t)s * N * H + n * H + h) * DK * W;
-    __syncthreads();  // previous X complete, previous readers of sM done
-    for (int e = tid; e < DK * DK / 4; e += 256) {
-      const int r = e / (DK / 4), c = (e - r * (DK / 4)) * 4;
-      *reinterpret_cast<f4*>(sM + r * LDM + c) = *reinterpret_cast<const f4*>(Sb + (int64_t)r * W + c);
+  f4 pf[NPF];
+  auto fetch = [&](int s) {
+    const float* Sb = summ(s);
+#pragma unroll
+    for (int q = 0; q < NPF; ++q) {
+      const int e = tid + 256 * q, r = e / (DK / 4), c = (e - r * (DK / 4)) * 4;
+      pf[q] = *reinterpret_cast<const f4*>(Sb + (int64_t)r * W + c);
     }
+  };
+  auto stash = [&](float* dst) {
+#pragma unroll
+    for (int q = 0; q < NPF; ++q) {
+      const int e = tid + 256 * q, r = e / (DK / 4), c = (e - r * (DK / 4)) * 4;
+      *reinterpret_cast<f4*>(dst + r * LDM + c) = pf[q];
+    }
+  };
+  fetch(seg_of(0));
+  stash(sM);
+  for (int it = 0; it < CP - 1; ++it) {
+    const int s = seg_of(it);
+    const int so = a.bwd ? s - 1 : s + 1;          // segment whose state is produced
+    const float* M = sM + (it & 1) * DK * LDM;
+    if (it + 1 < CP - 1) fetch(seg_of(it + 1));
     float acc[RPT];
+    const float* Sb = summ(s);
 #pragma unroll
     for (int r = 0; r < RPT; ++r) acc[r] = Sb[(int64_t)(r0 + r) * W + DK + dv0 + j];
-    __syncthreads();
+    __syncthreads();  // S in this buffer and X are complete
     for (int m = 0; m < DK; m += 4) {
-      const float x0 = sX[m * 64 + j], x1 = sX[(m + 1) * 64 + j];
-      const float x2 = sX[(m + 2) * 64 + j], x3 = sX[(m + 3) * 64 + j];
+      const float x0 = sX[m * 16 + j], x1 = sX[(m + 1) * 16 + j];
+      const float x2 = sX[(m + 2) * 16 + j], x3 = sX[(m + 3) * 16 + j];
 #pragma unroll
       for (int r = 0; r < RPT; ++r) {
-        const f4 mv = *reinterpret_cast<const f4*>(sM + (r0 + r) * LDM + m);
+        const f4 mv = *reinterpret_cast<const f4*>(M + (r0 + r) * LDM + m);
         acc[r] = fmaf(mv[0], x0, acc[r]);
         acc[r] = fmaf(mv[1], x1, acc[r]);
         acc[r] = fmaf(mv[2], x2, acc[r]);
         acc[r] = fmaf(mv[3], x3, acc[r]);
       }
     }
-    __syncthreads();  // all reads of X done
+    __syncthreads();  // all reads of X and of this S buffer done
+    if (it + 1 < CP - 1) stash(sM + ((it + 1) & 1) * DK * LDM);
     float* ob = a.out + ((int64_t)so * N * H + n * H + h) * DK * DV;
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
-      sX[(r0 + r) * 64 + j] = acc[r];
+      sX[(r0 + r) * 16 + j] = acc[r];
       ob[(int64_t)(r0 + r) * DV + dv0 + j] = acc[r];
     }
   }
@@ -775,10 +796,10 @@ hipError_t launch_scan_fwd(const ScanFwdArgs& a, bool f32, int hs_dtype, int DK,
 
 template <int DK>
 static hipError_t launch_cp_chain_t(const CpChainArgs& a, hipStream_t st) {
-  const size_t sm = (size_t)(DK * (DK + 4) + DK * 64) * sizeof(float);
+  const size_t sm = (size_t)(2 * DK * (DK + 4) + DK * 16) * sizeof(float);
   hipError_t e = hipFuncSetAttribute((const void*)k_cp_chain<DK>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_cp_chain<DK>, dim3(a.geo.N * a.geo.H, a.DV / 64), dim3(256), sm, st, a);
+  hipLaunchKernelGGL(k_cp_chain<DK>, dim3(a.geo.N * a.geo.H, a.DV / 16), dim3(256), sm, st, a);
   return hipGetLastError();
 }
 
