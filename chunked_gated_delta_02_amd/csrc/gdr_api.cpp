@@ -110,13 +110,13 @@ Plan make_plan(const gdr_problem* p, int mode, bool need_hs) {
     pl.Pf = take(ch * 64 * 64 * e);
     if (!pl.f32) pl.Pfl = take(ch * 64 * 64 * e);
   } else {
-    pl.Tm = take(ch * 64 * 64 * 4);
+    pl.Tm = take(ch * 64 * 64 * e);
     pl.WTf = take(ch * DK * 64 * e);
     pl.Kf = take(ch * 64 * DK * e);
     pl.dDl = take(ch * 64 * DV * 4);
     pl.Z = take(ch * DK * DV * 4);
     pl.dhs = take(ch * DK * DV * e);
-    pl.dD = take(ch * 64 * DV * 4);
+    pl.dD = take(ch * 64 * DV * e);
   }
   if (p->cp_segments > 1) {
     const size_t units = (size_t)p->cp_segments * pl.N * p->heads;
@@ -291,7 +291,7 @@ gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, con
     wa.q = q; wa.k = k; wa.v = v; wa.dO = dO; wa.beta = beta; wa.g = g;
     wa.gam = (float*)(ws + pl.gam); wa.Wf = ws + pl.Wf; wa.Ua = (float*)(ws + pl.Ua);
     wa.KtTf = h_saved ? nullptr : (void*)(ws + pl.KtTf);
-    wa.Tm = (float*)(ws + pl.Tm); wa.WTf = ws + pl.WTf; wa.Kf = ws + pl.Kf;
+    wa.Tm = ws + pl.Tm; wa.WTf = ws + pl.WTf; wa.Kf = ws + pl.Kf;
     wa.dDl = (float*)(ws + pl.dDl); wa.Z = (float*)(ws + pl.Z);
     GDR_LAUNCH(GDR_KERNEL_WY, s, gdr::launch_wy(wa, pl.f32, p->dk, true, s));
     if (!h_saved) {
@@ -311,7 +311,7 @@ gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, con
   gdr::ScanBwdArgs ba{};
   ba.geo = geo; ba.DV = p->dv; ba.layout = p->layout; ba.dhT = dhT; ba.dh0 = dh0;
   ba.gam = (const float*)(ws + pl.gam); ba.Kf = ws + pl.Kf; ba.WTf = ws + pl.WTf;
-  ba.dDl = (const float*)(ws + pl.dDl); ba.Z = (const float*)(ws + pl.Z); ba.dhs = ws + pl.dhs; ba.dD = (float*)(ws + pl.dD);
+  ba.dDl = (const float*)(ws + pl.dDl); ba.Z = (const float*)(ws + pl.Z); ba.dhs = ws + pl.dhs; ba.dD = ws + pl.dD;
   if (p->cp_segments > 1) {
     // the forward recompute above is done with the hand-off buffer: reuse it
     ba.summ = (float*)(ws + pl.summ); ba.dhend = (const float*)(ws + pl.hst);
@@ -324,8 +324,8 @@ gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, con
     gdr::GradArgs ga{};
     ga.geo = geo; ga.DV = p->dv; ga.scale = scale;
     ga.q = q; ga.k = k; ga.v = v; ga.dO = dO; ga.beta = beta;
-    ga.gam = (const float*)(ws + pl.gam); ga.Wf = ws + pl.Wf; ga.Ua = (const float*)(ws + pl.Ua); ga.Tm = (const float*)(ws + pl.Tm);
-    ga.hs = hs; ga.dhs = ws + pl.dhs; ga.dD = (const float*)(ws + pl.dD);
+    ga.gam = (const float*)(ws + pl.gam); ga.Wf = ws + pl.Wf; ga.Ua = (const float*)(ws + pl.Ua); ga.Tm = ws + pl.Tm;
+    ga.hs = hs; ga.dhs = ws + pl.dhs; ga.dD = ws + pl.dD;
     ga.dq = dq; ga.dk = dk; ga.dv = dv; ga.dbeta = dbeta; ga.dg = dg;
     GDR_LAUNCH(GDR_KERNEL_GRAD, s, gdr::launch_grad(ga, pl.f32, p->h_store_dtype, p->dk, s));
   }

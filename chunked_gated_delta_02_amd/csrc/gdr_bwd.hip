@@ -42,7 +42,8 @@ namespace gdr {
 // -dDelta^T goes to LDS as a split operand.  The per-chunk operands (K,
 // W^T, the two fp32 terms, the gate factors) are loaded raw into a ring of
 // SCAN_STAGES register sets, SCAN_STAGES - 1 chunks ahead.  Writes the dh
-// snapshot (io dtype) and dDelta (fp32), both in accumulator order, and dh0.
+// snapshot and dDelta (io dtype; the gradient kernel rounds its MFMA
+// operands to it anyway), both in accumulator order, and dh0.
 //   MODE 1: the reverse scan proper.
 //   MODE 0: CP segment summary -- scans the augmented gradient [I | 0] of
 //           width DK + DV backwards over one segment (the identity columns
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(256) void k_scan_bwd(const ScanBwdArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       acc_d[nt] = acc_d[nt] * o.ee + (mtile ? zero4() : o.dl[nt]);
-      if constexpr (MODE != 0) store_acc4(a.dD + ch * 64 * DV + acc_off(w, dv0 / 16 + nt, DV), acc_d[nt]);
+      if constexpr (MODE != 0) store_acc4((T*)a.dD + ch * 64 * DV + acc_off(w, dv0 / 16 + nt, DV), acc_d[nt]);
       store_acc_t2(sDD, sDDl, LDD, rw, 16 * nt, -acc_d[nt]);
     }
     __syncthreads();  // -dDelta^T complete; all readers of dh^T are done
@@ -248,7 +249,7 @@ __global__ __launch_bounds__(256) void k_scan_bwd(const ScanBwdArgs a) {
 // stay inside one wavefront; column sums go through per-wave LDS partials
 // reduced in a fixed order.
 template <typename T, typename HS, int DK>
-__global__ __launch_bounds__(256, 2) void k_grad(const GradArgs a) {
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const GradArgs a) {
   constexpr bool SPLIT = sizeof(T) == 2;
   constexpr int P = pad_of<T>();
   constexpr int LDK = DK + P;
@@ -302,7 +303,18 @@ __global__ __launch_bounds__(256, 2) void k_grad(const GradArgs a) {
     seg[tid] = a.gam[ch * GSTRIDE + 64 + tid];
     sE[tid] = a.gam[ch * GSTRIDE + 128 + tid];
   }
-  for (int e = tid; e < 64 * 64; e += 256) sT[(e >> 6) * L64 + (e & 63)] = from_f32<T>(a.Tm[ch * 4096 + e]);
+  {
+    // T (io dtype, row-major) -> operand copy in LDS; all loads issued first
+    typedef T t4 __attribute__((ext_vector_type(4)));
+    t4 tv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) tv[q] = *reinterpret_cast<const t4*>((const T*)a.Tm + ch * 4096 + 4 * (tid + 256 * q));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = 4 * (tid + 256 * q);
+      *reinterpret_cast<t4*>(sT + (e >> 6) * L64 + (e & 63)) = tv[q];
+    }
+  }
   const int rw = 16 * w;            // first output row of this wave
   const int r0 = rw + acc_row0();   // lane's rows r0..r0+3
 
@@ -327,40 +339,65 @@ __global__ __launch_bounds__(256, 2) void k_grad(const GradArgs a) {
 
   const int64_t rowq = (int64_t)t0 * H + h;   // token-row index of chunk row 0
   for (int dvb = 0; dvb < DV; dvb += DVB) {
+    f32x4 aD[NTB];          // Delta block = U - W h (rows 16w), starts as U
+    frag dof[DVB / KW];     // dO fragments (rows 16w, k = dv)
     __syncthreads();
     // h and dh (accumulator order <DK, DV>) and dDelta (accumulator order
     // <64, DV>) of this DV block, transposed into (dv, .) rows in LDS;
     // <dh, h> (for e^{gamma_L} <dh, h>) uses h in its stored precision
     {
+      // all global loads of this block are issued before the first LDS store
       const HS* hb = (const HS*)a.hs + ch * DK * DV;
       const T* db = (const T*)a.dhs + ch * DK * DV;
-      for (int e = tid; e < (DK / 16) * NTB * 64; e += 256) {
-        const int ll = e & 63, tt = e >> 6;
+      const T* ddb = (const T*)a.dD + ch * 64 * DV;
+      constexpr int IH = (DK / 16) * NTB * 64 / 256, ID = 4 * NTB * 64 / 256;
+      typedef T t4 __attribute__((ext_vector_type(4)));
+      f32x4 hv[IH];
+      t4 gv[IH], dv4[ID];   // dh snapshot and dDelta, io dtype
+      {
+        const float* Ub = a.Ua + ch * 64 * DV;
+#pragma unroll
+        for (int nt = 0; nt < NTB; ++nt) aD[nt] = load4f(Ub + acc_off(w, dvb / 16 + nt, DV));
+#pragma unroll
+        for (int ks = 0; ks < DVB / KW; ++ks)
+          dof[ks] = frag_rowk_masked(dop + rowq * DV + dvb, (int64_t)H * DV, rw, ks * KW, len);
+      }
+#pragma unroll
+      for (int q = 0; q < IH; ++q) {
+        const int e = tid + 256 * q, ll = e & 63, tt = e >> 6;
         const int m = tt / NTB, nn = tt - m * NTB;
         const int64_t off = acc_off_l(m, dvb / 16 + nn, DV, ll);
-        const int dk = 16 * m + 4 * (ll >> 4), dvl = 16 * nn + (ll & 15);
-        const f32x4 hv = load4f(hb + off);
-        const f32x4 gv = load4f(db + off);
-        gLh += hv[0] * gv[0] + hv[1] * gv[1] + hv[2] * gv[2] + hv[3] * gv[3];
-        store_acc4(sHvk + dvl * LDK + dk, hv);
-        store_acc4(sDHvk + dvl * LDK + dk, gv);
+        hv[q] = load4f(hb + off);
+        gv[q] = *reinterpret_cast<const t4*>(db + off);
       }
-      const float* ddb = a.dD + ch * 64 * DV;
-      for (int e = tid; e < 4 * NTB * 64; e += 256) {
-        const int ll = e & 63, tt = e >> 6;
+#pragma unroll
+      for (int q = 0; q < ID; ++q) {
+        const int e = tid + 256 * q, ll = e & 63, tt = e >> 6;
+        const int m = tt / NTB, nn = tt - m * NTB;
+        dv4[q] = *reinterpret_cast<const t4*>(ddb + acc_off_l(m, dvb / 16 + nn, DV, ll));
+      }
+#pragma unroll
+      for (int q = 0; q < IH; ++q) {
+        const int e = tid + 256 * q, ll = e & 63, tt = e >> 6;
+        const int m = tt / NTB, nn = tt - m * NTB;
+        const int dk = 16 * m + 4 * (ll >> 4), dvl = 16 * nn + (ll & 15);
+        const f32x4 g4 = {to_f32(gv[q][0]), to_f32(gv[q][1]), to_f32(gv[q][2]), to_f32(gv[q][3])};
+        gLh += hv[q][0] * g4[0] + hv[q][1] * g4[1] + hv[q][2] * g4[2] + hv[q][3] * g4[3];
+        store_acc4(sHvk + dvl * LDK + dk, hv[q]);
+        *reinterpret_cast<t4*>(sDHvk + dvl * LDK + dk) = gv[q];
+      }
+#pragma unroll
+      for (int q = 0; q < ID; ++q) {
+        const int e = tid + 256 * q, ll = e & 63, tt = e >> 6;
         const int m = tt / NTB, nn = tt - m * NTB;
         const int r = 16 * m + 4 * (ll >> 4), dvl = 16 * nn + (ll & 15);
-        store_acc4(sDDt + dvl * L64 + r, load4f(ddb + acc_off_l(m, dvb / 16 + nn, DV, ll)));
+        *reinterpret_cast<t4*>(sDDt + dvl * L64 + r) = dv4[q];
       }
     }
     load_rows<T, DVB>(sV, LDV, vp + rowq * DV + dvb, (int64_t)H * DV, len);
     __syncthreads();
     // Delta block = U - W h  (rows 16w)
-    f32x4 aD[NTB];
     {
-      const float* Ub = a.Ua + ch * 64 * DV;
-#pragma unroll
-      for (int nt = 0; nt < NTB; ++nt) aD[nt] = load4f(Ub + acc_off(w, dvb / 16 + nt, DV));
 #pragma unroll
       for (int ks = 0; ks < DK / KW; ++ks)
 #pragma unroll
@@ -369,11 +406,6 @@ __global__ __launch_bounds__(256, 2) void k_grad(const GradArgs a) {
 #pragma unroll
       for (int nt = 0; nt < NTB; ++nt) store_acc_t2(sDeltaT, sDeltaTl, L64, rw, 16 * nt, aD[nt]);
     }
-    // dO fragments (rows 16w, k = dv)
-    frag dof[DVB / KW];
-#pragma unroll
-    for (int ks = 0; ks < DVB / KW; ++ks)
-      dof[ks] = frag_rowk_masked(dop + rowq * DV + dvb, (int64_t)H * DV, rw, ks * KW, len);
     // dQg += dO h^T ; dW -= dDelta h^T ; dT_V += dDelta V^T
 #pragma unroll
     for (int ks = 0; ks < DVB / KW; ++ks) {

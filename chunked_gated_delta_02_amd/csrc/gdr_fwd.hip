@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
   T* sW = (T*)ra;                         // W (r, dk) staging
   T* sQ = (T*)ra;                         // Q (r, dk), after W is written
   float* sTm = (float*)(ra + RA);         // T (fp32), until U is done
-  float* sPT = sTm;                       // then P^T (s, r) fp32
+  float* sPT = sTm;                       // then P (r, s) (forward) or P^T (s, r) (backward), fp32
   T* sV = (T*)(ra + RA + 64 * LDF * 4);   // V / dO block (r, dv)
   float* sX = (float*)(sV + 64 * LDV);
   float* sg = sX + 4 * 16 * 20;
@@ -225,7 +225,12 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
     __syncthreads();
   }
   if constexpr (BWD) {
-    for (int e = tid; e < 64 * 64; e += 256) a.Tm[ch * 4096 + e] = sTm[(e >> 6) * LDF + (e & 63)];
+    // T in the io dtype, row-major: the gradient kernel's operand copy
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = 4 * (tid + 256 * q);
+      store_acc4((T*)a.Tm + ch * 4096 + e, *reinterpret_cast<const f32x4*>(sTm + (e >> 6) * LDF + (e & 63)));
+    }
   }
 
   // W^T = K^T (T diag(beta e^gamma))^T (DK x 64): wave w owns dk rows
@@ -262,13 +267,12 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
       for (int nt = 0; nt < 4; ++nt) store_acc_t(sW, LDK, w * (DK / 4) + 16 * mt, 16 * nt, acc[mt][nt]);
   }
   __syncthreads();
-  write_afrag<T, 64, DK>((T*)a.Wf + ch * 64 * DK, [&](int i, int k) { return to_f32(sW[i * LDK + k]); });
+  copy_afrag<T, 64, DK, false>((T*)a.Wf + ch * 64 * DK, sW, LDK);
   if constexpr (BWD) {
-    write_afrag<T, DK, 64>((T*)a.WTf + ch * DK * 64, [&](int i, int k) { return to_f32(sW[k * LDK + i]); });
-    write_afrag<T, 64, DK>((T*)a.Kf + ch * 64 * DK, [&](int i, int k) { return to_f32(sK[i * LDK + k]); });
+    copy_afrag<T, DK, 64, true>((T*)a.WTf + ch * DK * 64, sW, LDK);
+    copy_afrag<T, 64, DK, false>((T*)a.Kf + ch * 64 * DK, sK, LDK);
   }
-  if (a.KtTf)
-    write_afrag<T, DK, 64>((T*)a.KtTf + ch * DK * 64, [&](int i, int k) { return to_f32(sK[k * LDK + i]); });
+  if (a.KtTf) copy_afrag<T, DK, 64, true>((T*)a.KtTf + ch * DK * 64, sK, LDK);
 
   // U = T diag(beta) V per DV block (rows 16w, fp32, accumulator order);
   // T diag(beta) is a split operand read from the fp32 T
@@ -301,22 +305,26 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
   __syncthreads();  // W staging, T and V are dead from here
   load_rows<T, DK>(sQ, LDK, (const T*)a.q + rowq * DK, (int64_t)H * DK, len);
   __syncthreads();
-  // P^T = K Q^T * Gam^T (rows s = 16w, diagonal included), staged fp32
+  // forward: P = Q K^T * Gam (rows r = 16w); backward: P^T (rows s = 16w);
+  // diagonal included, staged fp32 in its own orientation
   {
     f32x4 acc[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) acc[nt] = zero4();
+    const T* sA1 = BWD ? sK : sQ;
+    const T* sB1 = BWD ? sQ : sK;
 #pragma unroll
     for (int ks = 0; ks < DK; ks += KW) {
-      const auto af = frag_rowk(sK, LDK, 16 * w, ks);
+      const auto af = frag_rowk(sA1, LDK, 16 * w, ks);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[nt] = Mma<T>::mma(af, frag_rowk(sQ, LDK, 16 * nt, ks), acc[nt]);
+      for (int nt = 0; nt < 4; ++nt) acc[nt] = Mma<T>::mma(af, frag_rowk(sB1, LDK, 16 * nt, ks), acc[nt]);
     }
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int s = 16 * w + acc_row0() + i, r = 16 * nt + acc_col();
+        const int x = 16 * w + acc_row0() + i, y = 16 * nt + acc_col();
+        const int r = BWD ? y : x, s = BWD ? x : y;
         acc[nt][i] = (s <= r) ? acc[nt][i] * expf(sg[r] - sg[s]) : 0.f;
       }
       store_acc(sPT, LDF, 16 * w, 16 * nt, acc[nt]);
@@ -324,9 +332,8 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
   }
   __syncthreads();
   if constexpr (!BWD) {
-    write_afrag<T, 64, 64>((T*)a.Pf + ch * 4096, [&](int i, int k) { return sPT[k * LDF + i]; },
-                           SPLIT ? (T*)a.Pfl + ch * 4096 : nullptr);
-    write_afrag<T, 64, DK>((T*)a.Qf + ch * 64 * DK, [&](int i, int k) { return to_f32(sQ[i * LDK + k]); });
+    copy_afrag_split<T, 64, 64>((T*)a.Pf + ch * 4096, SPLIT ? (T*)a.Pfl + ch * 4096 : nullptr, sPT, LDF);
+    copy_afrag<T, 64, DK, false>((T*)a.Qf + ch * 64 * DK, sQ, LDK);
   } else {
     // per DV block of dO: scale P^T dO (rows s = 16w) and scale Qg^T dO
     // (rows dk: wave w owns [w DK/4, (w+1) DK/4)), fp32, accumulator order;

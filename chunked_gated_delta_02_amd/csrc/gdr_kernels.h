@@ -48,7 +48,7 @@ struct WyArgs {
   void* Qf;     // afrag<64, DK>: Q (exact)                          (forward)
   void* Pf;     // afrag<64, 64>: P = Q K^T * Gam (rows r), hi part  (forward)
   void* Pfl;    // the lo part (bf16 only)                           (forward)
-  float* Tm;    // [64][64] fp32 row-major: T                       (backward)
+  void* Tm;     // [64][64] row-major (io dtype): T                 (backward)
   void* WTf;    // afrag<DK, 64>: W^T                                (backward)
   void* Kf;     // afrag<64, DK>: K (exact)                          (backward)
   float* dDl;   // acc<64, DV> fp32: scale P^T dO                    (backward)
@@ -95,7 +95,7 @@ struct ScanBwdArgs {
   const float* dDl;
   const float* Z;
   void* dhs;         // acc<DK, DV> (io dtype): gradient of the state at chunk end
-  float* dD;         // acc<64, DV> fp32: gradient of Delta
+  void* dD;          // acc<64, DV> (io dtype): gradient of Delta
 };
 
 // Hand-off of the CP segment states, per (sequence, head, 64-column tile):
@@ -124,10 +124,10 @@ struct GradArgs {
   const float* gam;
   const void* Wf;
   const float* Ua;
-  const float* Tm;
+  const void* Tm;
   const void* hs;
   const void* dhs;
-  const float* dD;
+  const void* dD;
   void* dq;
   void* dk;
   void* dv;
@@ -136,41 +136,31 @@ struct GradArgs {
 };
 
 // ---------------------------------------------------------------------------
-// LDS staging.  NR rows of NC elements from global (row stride gstride
-// elements) into LDS (row stride ld); rows >= nvalid are zero.  16-byte
-// accesses, all 256 threads.
+// LDS staging (workgroups of 256 threads).  NR rows of NC elements from
+// global (row stride gstride elements) into LDS (row stride ld); rows >=
+// nvalid are zero.  16-byte accesses.  All of a thread's loads are issued
+// before its first LDS store (compile-time trip count), so their latencies
+// overlap instead of adding up.
 template <typename T, int NC, int NR = 64>
 __device__ __forceinline__ void load_rows(T* s, int ld, const T* g, int64_t gstride, int nvalid) {
   constexpr int VEC = 16 / sizeof(T);
   constexpr int PER_ROW = NC / VEC;
+  constexpr int NP = NR * PER_ROW;
+  constexpr int IT = (NP + 255) / 256;
   typedef float f4 __attribute__((ext_vector_type(4)));
-  for (int e = threadIdx.x; e < NR * PER_ROW; e += blockDim.x) {
+  f4 v[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int e = threadIdx.x + 256 * it;
     const int r = e / PER_ROW, c = (e - r * PER_ROW) * VEC;
-    f4 v = {0.f, 0.f, 0.f, 0.f};
-    if (r < nvalid) v = *reinterpret_cast<const f4*>(g + r * gstride + c);
-    *reinterpret_cast<f4*>(s + r * ld + c) = v;
+    v[it] = (f4){0.f, 0.f, 0.f, 0.f};
+    if (e < NP && r < nvalid) v[it] = *reinterpret_cast<const f4*>(g + r * gstride + c);
   }
-}
-
-// Same with element conversion from S (global) to T (LDS).
-template <typename S, typename T, int NC, int NR>
-__device__ __forceinline__ void load_rows_conv(T* s, int ld, const S* g, int64_t gstride, int nvalid) {
-  if constexpr (__is_same(S, T)) {
-    load_rows<T, NC, NR>(s, ld, (const T*)g, gstride, nvalid);
-  } else {
-    constexpr int VEC = 4;
-    constexpr int PER_ROW = NC / VEC;
-    for (int e = threadIdx.x; e < NR * PER_ROW; e += blockDim.x) {
-      const int r = e / PER_ROW, c = (e - r * PER_ROW) * VEC;
-      float v[4] = {0.f, 0.f, 0.f, 0.f};
-      if (r < nvalid) {
-        const S* q = g + r * gstride + c;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = to_f32(q[j]);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) s[r * ld + c + j] = from_f32<T>(v[j]);
-    }
+  for (int it = 0; it < IT; ++it) {
+    const int e = threadIdx.x + 256 * it;
+    const int r = e / PER_ROW, c = (e - r * PER_ROW) * VEC;
+    if (e < NP) *reinterpret_cast<f4*>(s + r * ld + c) = v[it];
   }
 }
 
@@ -222,6 +212,40 @@ __device__ __forceinline__ void write_afrag(T* dst, F&& f, T* dlo = nullptr) {
     } else {
       *reinterpret_cast<f32x4*>(dst + (int64_t)p * PE) = (f32x4){v[0], v[1], v[2], v[3]};
     }
+  }
+}
+
+// Copy an R x K matrix from LDS into afrag<R, K> order, one MFMA fragment
+// (64 lanes x 16 bytes for bf16) per wave step: element (i, k) is
+// src[i * ld + k] (RowK) or src[k * ld + i] (ColK).  4 waves.
+template <typename T, int R, int K, bool COLK>
+__device__ __forceinline__ void copy_afrag(T* dst, const T* src, int ld) {
+  constexpr int KW = Mma<T>::KW, KPL = Mma<T>::KPL;
+  constexpr int NF = (R / 16) * (K / KW);
+  typedef typename Mma<T>::frag frag;
+#pragma unroll
+  for (int f = wave_id(); f < NF; f += 4) {
+    const int m = f / (K / KW), s = f - m * (K / KW);
+    const frag v = COLK ? frag_colk_lds(src, ld, 16 * m, s * KW) : frag_rowk(src, ld, 16 * m, s * KW);
+    *reinterpret_cast<frag*>(dst + ((int64_t)f * 64 + lane_id()) * KPL) = v;
+  }
+}
+
+// Same for an fp32 LDS matrix (RowK, row stride ld, 16-byte aligned rows)
+// written as a split pair: hi into dst, lo into dlo (fp32 operands: dst only).
+template <typename T, int R, int K>
+__device__ __forceinline__ void copy_afrag_split(T* dst, T* dlo, const float* src, int ld) {
+  constexpr int KW = Mma<T>::KW, KPL = Mma<T>::KPL;
+  constexpr int NF = (R / 16) * (K / KW);
+  typedef typename Mma<T>::frag frag;
+  auto one = [](int) { return 1.f; };
+#pragma unroll
+  for (int f = wave_id(); f < NF; f += 4) {
+    const int m = f / (K / KW), s = f - m * (K / KW);
+    frag hi, lo;
+    frag_rowk_f32<T>(src, ld, 16 * m, s * KW, one, hi, lo);
+    *reinterpret_cast<frag*>(dst + ((int64_t)f * 64 + lane_id()) * KPL) = hi;
+    if constexpr (sizeof(T) == 2) *reinterpret_cast<frag*>(dlo + ((int64_t)f * 64 + lane_id()) * KPL) = lo;
   }
 }
 
