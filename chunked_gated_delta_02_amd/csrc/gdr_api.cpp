@@ -150,8 +150,11 @@ gdr::Geo make_geo(const gdr_problem* p, const Plan& pl, const int32_t* cu, char*
 // scans run one or two per CU), among the tiles that fit in registers
 // without spilling (64 only with DK = 64).  The fp32 path always uses 16
 // (its operand fragments are 8x larger per k).
-int pick_dvt(long units, int cols, bool f32, int dk) {
+// The output scan (8 waves, two roles) fits in registers only up to
+// 32 columns at DK = 64 and 16 at DK = 128.
+int pick_dvt(long units, int cols, bool f32, int dk, bool out = false) {
   if (f32) return 16;
+  if (out) return (dk == 64 && units * (cols / 32) >= 256) ? 32 : 16;
   if (dk == 64 && units * (cols / 64) >= 256) return 64;
   if (units * (cols / 32) >= 256) return 32;
   return 16;
@@ -248,7 +251,7 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, con
     gdr::CpChainArgs ca{geo, p->dk, p->dv, p->layout, 0, h0, (const float*)(ws + pl.summ), (float*)(ws + pl.hst)};
     GDR_LAUNCH(GDR_KERNEL_CP_CHAIN_FWD, s, gdr::launch_cp_chain(ca, s));
   }
-  GDR_LAUNCH(GDR_KERNEL_SCAN_FWD, s, gdr::launch_scan_fwd(sa, pl.f32, p->h_store_dtype, p->dk, pick_dvt(units, p->dv, pl.f32, p->dk), 2, s));
+  GDR_LAUNCH(GDR_KERNEL_SCAN_FWD, s, gdr::launch_scan_fwd(sa, pl.f32, p->h_store_dtype, p->dk, pick_dvt(units, p->dv, pl.f32, p->dk, true), 2, s));
   return GDR_OK;
 }
 

@@ -153,6 +153,12 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
     a.gam[ch * GSTRIDE + 128 + l] = eE;
   }
   load_rows<T, DK>(sK, LDK, kp + rowq * DK, (int64_t)H * DK, len);
+  // the other inputs are fetched into registers now, so their latency
+  // overlaps the construction of T; each is stored to LDS when needed
+  RowBuf<T, DK> qbuf;
+  RowBuf<T, DVB> vbuf;
+  qbuf.load((const T*)a.q + rowq * DK, (int64_t)H * DK, len);
+  vbuf.load(vp + rowq * DV, (int64_t)H * DV, len);
   __syncthreads();
 
   // A = strictly_lower(diag(beta) K K^T * Gam): rows 16w, 4 column tiles
@@ -280,7 +286,9 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
     auto d2 = [&](int s) { return sb[s]; };
     for (int dv0 = 0; dv0 < DV; dv0 += DVB) {
       __syncthreads();
-      load_rows<T, DVB>(sV, LDV, vp + rowq * DV + dv0, (int64_t)H * DV, len);
+      vbuf.store(sV, LDV);
+      if (dv0 + DVB < DV) vbuf.load(vp + rowq * DV + dv0 + DVB, (int64_t)H * DV, len);
+      else if constexpr (BWD) vbuf.load((const T*)a.dO + rowq * DV, (int64_t)H * DV, len);   // first dO block
       __syncthreads();
       f32x4 acc[DVB / 16];
 #pragma unroll
@@ -303,7 +311,7 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
   }
 
   __syncthreads();  // W staging, T and V are dead from here
-  load_rows<T, DK>(sQ, LDK, (const T*)a.q + rowq * DK, (int64_t)H * DK, len);
+  qbuf.store(sQ, LDK);
   __syncthreads();
   // forward: P = Q K^T * Gam (rows r = 16w); backward: P^T (rows s = 16w);
   // diagonal included, staged fp32 in its own orientation
@@ -345,7 +353,8 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
     constexpr int MT = DK / 64;
     for (int dv0 = 0; dv0 < DV; dv0 += DVB) {
       __syncthreads();
-      load_rows<T, DVB>(sV, LDV, dop + rowq * DV + dv0, (int64_t)H * DV, len);
+      vbuf.store(sV, LDV);
+      if (dv0 + DVB < DV) vbuf.load(dop + rowq * DV + dv0 + DVB, (int64_t)H * DV, len);
       __syncthreads();
       f32x4 accp[DVB / 16], accz[MT][DVB / 16];
 #pragma unroll
@@ -386,16 +395,20 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
 
 // ---------------------------------------------------------------------------
 // k_scan_fwd: per (unit, column tile).  Serial over the unit's chunks.  The
-// state tile h (DK x DVT, fp32) is held in MFMA accumulators (wave w owns dk
-// rows [w DK/4, (w+1) DK/4)); h^T lives in LDS as a split operand (hi, lo)
-// for W h and Q h.  Delta = U - W h and E Delta (E = e^{gamma_L - gamma})
-// go to LDS as split operands of P Delta and of the update
-// h <- e^{gamma_L} h + K^T (E Delta).  All per-chunk operands that do not
-// depend on h (W, K^T, U, Q, P, the gate factors) are loaded raw into a ring
-// of SCAN_STAGES register sets, SCAN_STAGES - 1 chunks ahead; nothing
-// touches a loaded value before its chunk is processed, so the loads stay in
-// flight while earlier chunks run.
-//   MODE 2: writes the snapshots and o = scale (e^gamma (Q h) + P Delta);
+// state tile h (DK x DVT, fp32) is held in MFMA accumulators of waves 0..3
+// (wave w owns dk rows [w DK/4, (w+1) DK/4)); h^T lives in LDS as a split
+// operand (hi, lo) for W h and Q h.  Delta = U - W h and E Delta
+// (E = e^{gamma_L - gamma}) go to LDS as split operands of P Delta and of
+// the update h <- e^{gamma_L} h + K^T (E Delta).  All per-chunk operands
+// that do not depend on h are loaded raw into a ring of SCAN_STAGES register
+// sets, SCAN_STAGES - 1 chunks ahead; nothing touches a loaded value before
+// its chunk is processed, so the loads stay in flight while earlier chunks
+// run.
+//   MODE 2: 8 waves.  Waves 0..3 run the recurrence and write the
+//           snapshots; waves 4..7 compute o = scale (e^gamma (Q h) + P Delta)
+//           beside them from double-buffered copies of h^T and Delta^T, so
+//           the output is off the recurrence's critical path.  Both roles
+//           meet at the same two barriers per chunk.
 //   MODE 1: writes the snapshots only (backward recompute);
 //   MODE 0: CP segment summary -- scans the augmented state [I | 0] of width
 //           DK + DV over one segment (the identity columns take U = 0, so
@@ -406,7 +419,7 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
 #define SCAN_STAGES 3
 
 template <typename T, typename HS, int DK, int DVT, int MODE>
-__global__ __launch_bounds__(256) void k_scan_fwd(const ScanFwdArgs a) {
+__global__ __launch_bounds__(MODE == 2 ? 512 : 256) void k_scan_fwd(const ScanFwdArgs a) {
   constexpr bool OUT = MODE == 2;
   constexpr bool SPLIT = sizeof(T) == 2;
   constexpr int P = pad_of<T>();
@@ -417,18 +430,22 @@ __global__ __launch_bounds__(256) void k_scan_fwd(const ScanFwdArgs a) {
   constexpr int KS64 = 64 / KW;
   constexpr int MTH = DK / 64;
   constexpr int NT = DVT / 16;
-  // ring depth: fp32 fragments are 8x larger, and the output operands of
-  // MODE 2 double the per-chunk set
-  constexpr int S = sizeof(T) == 2 ? (MODE != 2 ? SCAN_STAGES : 2) : (MODE != 2 ? 2 : 1);
+  constexpr int NB = OUT ? 2 : 1;   // h^T / Delta^T buffers
+  // fp32 fragments are 8x larger: shallower ring
+  constexpr int S = sizeof(T) == 2 ? (OUT ? 2 : SCAN_STAGES) : (OUT ? 1 : 2);
+  // raw operand slots per ring stage, shared by both roles
+  constexpr int NXR = KS + MTH * KS64;            // W, K^T
+  constexpr int NXO = KS + (SPLIT ? 2 : 1) * KS64;  // Q, P (hi, lo)
+  constexpr int NX = OUT ? cmax(NXR, NXO) : NXR;
   typedef typename Mma<T>::frag frag;
   constexpr int LDO = DVT + P;
-  __shared__ __align__(16) T sH[DVT * LDH];                   // h^T (dv, dk), hi
-  __shared__ __align__(16) T sHl[SPLIT ? DVT * LDH : 1];      // lo
-  __shared__ __align__(16) T sDE[DVT * LDD];                  // (E Delta)^T (dv, r), hi
+  __shared__ __align__(16) T sH[NB][DVT * LDH];                   // h^T (dv, dk), hi
+  __shared__ __align__(16) T sHl[NB][SPLIT ? DVT * LDH : 1];      // lo
+  __shared__ __align__(16) T sDE[DVT * LDD];                      // (E Delta)^T (dv, r), hi
   __shared__ __align__(16) T sDEl[SPLIT ? DVT * LDD : 1];
-  __shared__ __align__(16) T sD[OUT ? DVT * LDD : 1];         // Delta^T (dv, r), hi
-  __shared__ __align__(16) T sDl[OUT && SPLIT ? DVT * LDD : 1];
-  __shared__ __align__(16) T sO[OUT ? 64 * LDO : 1];          // output staging (each wave: its rows)
+  __shared__ __align__(16) T sD[NB][OUT ? DVT * LDD : 1];         // Delta^T (dv, r), hi
+  __shared__ __align__(16) T sDl[NB][OUT && SPLIT ? DVT * LDD : 1];
+  __shared__ __align__(16) T sO[OUT ? 64 * LDO : 1];              // output staging
 
   const int H = a.geo.H, DV = a.DV, CP = a.geo.cp, N = a.geo.N;
   int p, jt;
@@ -440,7 +457,8 @@ __global__ __launch_bounds__(256) void k_scan_fwd(const ScanFwdArgs a) {
   const int dv0 = MODE == 0 ? (mtile ? 0 : col0 - DK) : col0;   // column of U (and o)
   int c0, nc, ts, tl;
   seg_range(a.geo, n, sg, c0, nc, ts, tl);
-  const int w = wave_id();
+  const bool orole = OUT && wave_id() >= 4;   // output waves
+  const int w = wave_id() & 3;                // row block of either role
   const int l = lane_id();
   const int dkw = w * (DK / 4);
   const int rw = 16 * w;
@@ -449,139 +467,155 @@ __global__ __launch_bounds__(256) void k_scan_fwd(const ScanFwdArgs a) {
   f32x4 acc_h[MTH][NT];
   const int64_t sb = (int64_t)(n * H + h) * DK * DV;
   const int64_t cpb = ((int64_t)sg * N * H + n * H + h) * DK;   // row 0 of this unit's CP tile
-#pragma unroll
-  for (int mt = 0; mt < MTH; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int dk = dkw + 16 * mt + acc_row0() + i, dv = dv0 + 16 * nt + acc_col();
-        float v = 0.f;
-        if (MODE == 0) v = (mtile && dk == col0 + 16 * nt + acc_col()) ? 1.f : 0.f;
-        else if (sg > 0) v = a.hstart[(cpb + dk) * DV + dv];
-        else if (a.h0) v = (a.layout == 0) ? a.h0[sb + (int64_t)dk * DV + dv] : a.h0[sb + (int64_t)dv * DK + dk];
-        acc_h[mt][nt][i] = v;
-      }
-#pragma unroll
-  for (int mt = 0; mt < MTH; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) store_acc_t2(sH, sHl, LDH, dkw + 16 * mt, 16 * nt, acc_h[mt][nt]);
-
-  struct Ops {
-    frag wf[KS];            // W rows 16w
-    frag kf[MTH][KS64];     // K^T rows dkw.., k = chunk row
-    f32x4 u[NT];            // U (fp32, accumulator order, raw)
-    frag qf[KS];            // Q rows 16w
-    frag pf[KS64];          // P rows 16w, hi
-    frag pl[KS64];          // P rows 16w, lo
-    f32x4 eg;               // e^gamma of the lane's 4 rows
-    f32x4 ee;               // e^{gamma_L - gamma} of the lane's 4 rows
-    float eL;               // e^{gamma_L}
-  };
-  auto load_ops = [&](int c, Ops& o) {
-    const int64_t ch = chb + c;
-    const T* Wb = (const T*)a.Wf + ch * 64 * DK;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) o.wf[ks] = frag_af<T, DK>(Wb, w, ks);
-    const T* Kb = (const T*)a.KtTf + ch * DK * 64;
+  if (!orole) {
 #pragma unroll
     for (int mt = 0; mt < MTH; ++mt)
 #pragma unroll
-      for (int ks = 0; ks < KS64; ++ks) o.kf[mt][ks] = frag_af<T, 64>(Kb, dkw / 16 + mt, ks);
-    const float* Ub = a.Ua + ch * 64 * DV;
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) o.u[nt] = *reinterpret_cast<const f32x4*>(Ub + acc_off(w, dv0 / 16 + nt, DV));
+        for (int i = 0; i < 4; ++i) {
+          const int dk = dkw + 16 * mt + acc_row0() + i, dv = dv0 + 16 * nt + acc_col();
+          float v = 0.f;
+          if (MODE == 0) v = (mtile && dk == col0 + 16 * nt + acc_col()) ? 1.f : 0.f;
+          else if (sg > 0) v = a.hstart[(cpb + dk) * DV + dv];
+          else if (a.h0) v = (a.layout == 0) ? a.h0[sb + (int64_t)dk * DV + dv] : a.h0[sb + (int64_t)dv * DK + dk];
+          acc_h[mt][nt][i] = v;
+        }
+#pragma unroll
+    for (int mt = 0; mt < MTH; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) store_acc_t2(sH[0], sHl[0], LDH, dkw + 16 * mt, 16 * nt, acc_h[mt][nt]);
+  }
+
+  // one ring stage: recurrence waves hold W (x[0, KS)), K^T (x[KS, ..)),
+  // U (v[0, NT)), E (v[NT]) and e^{gamma_L} (s); output waves hold Q
+  // (x[0, KS)), P hi (x[KS, KS + KS64)), P lo (after it) and e^gamma (v[NT])
+  struct Ops {
+    frag x[NX];
+    f32x4 v[NT + 1];
+    float s;
+  };
+  auto load_ops = [&](int c, Ops& o) {
+    const int64_t ch = chb + c;
     const float* gb = a.gam + ch * GSTRIDE;
-    o.ee = *reinterpret_cast<const f32x4*>(gb + 128 + rw + acc_row0());
-    o.eL = gb[64 + 63];
-    if constexpr (OUT) {
+    if (!orole) {
+      const T* Wb = (const T*)a.Wf + ch * 64 * DK;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) o.x[ks] = frag_af<T, DK>(Wb, w, ks);
+      const T* Kb = (const T*)a.KtTf + ch * DK * 64;
+#pragma unroll
+      for (int mt = 0; mt < MTH; ++mt)
+#pragma unroll
+        for (int ks = 0; ks < KS64; ++ks) o.x[KS + mt * KS64 + ks] = frag_af<T, 64>(Kb, dkw / 16 + mt, ks);
+      const float* Ub = a.Ua + ch * 64 * DV;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) o.v[nt] = *reinterpret_cast<const f32x4*>(Ub + acc_off(w, dv0 / 16 + nt, DV));
+      o.v[NT] = *reinterpret_cast<const f32x4*>(gb + 128 + rw + acc_row0());
+      o.s = gb[64 + 63];
+    } else if constexpr (OUT) {
       const T* Qb = (const T*)a.Qf + ch * 64 * DK;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) o.qf[ks] = frag_af<T, DK>(Qb, w, ks);
+      for (int ks = 0; ks < KS; ++ks) o.x[ks] = frag_af<T, DK>(Qb, w, ks);
       const T* Pb = (const T*)a.Pf + ch * 4096;
 #pragma unroll
-      for (int ks = 0; ks < KS64; ++ks) o.pf[ks] = frag_af<T, 64>(Pb, w, ks);
+      for (int ks = 0; ks < KS64; ++ks) o.x[KS + ks] = frag_af<T, 64>(Pb, w, ks);
       if constexpr (SPLIT) {
         const T* Pl = (const T*)a.Pfl + ch * 4096;
 #pragma unroll
-        for (int ks = 0; ks < KS64; ++ks) o.pl[ks] = frag_af<T, 64>(Pl, w, ks);
+        for (int ks = 0; ks < KS64; ++ks) o.x[KS + KS64 + ks] = frag_af<T, 64>(Pl, w, ks);
       }
-      o.eg = *reinterpret_cast<const f32x4*>(gb + 64 + rw + acc_row0());
+      o.v[NT] = *reinterpret_cast<const f32x4*>(gb + 64 + rw + acc_row0());
     }
   };
 
   auto process = [&](int c, Ops& o) {
     const int64_t ch = chb + c;
+    const int hb = OUT ? (c & 1) : 0;   // buffer holding h_c and Delta_c
     if constexpr (MODE != 0) {
-      HS* hb = (HS*)a.hs + ch * DK * DV;
+      if (!orole) {
+        HS* hsb = (HS*)a.hs + ch * DK * DV;
+#pragma unroll
+        for (int mt = 0; mt < MTH; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) store_acc4(hsb + acc_off(dkw / 16 + mt, dv0 / 16 + nt, DV), acc_h[mt][nt]);
+      }
+    }
+    __syncthreads();  // h^T of this chunk is complete
+    f32x4 acc_o[NT];
+    if (!orole) {
+      // Delta = U - W h (rows 16w)
+      f32x4 acc_d[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc_d[nt] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          acc_d[nt] = Mma<T>::mma(o.x[ks], frag_rowk(sH[hb], LDH, 16 * nt, ks * KW), acc_d[nt]);
+          if constexpr (SPLIT) acc_d[nt] = Mma<T>::mma(o.x[ks], frag_rowk(sHl[hb], LDH, 16 * nt, ks * KW), acc_d[nt]);
+        }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc_d[nt][i] = (mtile ? 0.f : o.v[nt][i]) - acc_d[nt][i];
+        store_acc_t2(sDE, sDEl, LDD, rw, 16 * nt, acc_d[nt] * o.v[NT]);
+        if constexpr (OUT) store_acc_t2(sD[hb], sDl[hb], LDD, rw, 16 * nt, acc_d[nt]);
+      }
+    } else if constexpr (OUT) {
+      // e^gamma (Q h) (rows 16w)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc_o[nt] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          acc_o[nt] = Mma<T>::mma(o.x[ks], frag_rowk(sH[hb], LDH, 16 * nt, ks * KW), acc_o[nt]);
+          if constexpr (SPLIT) acc_o[nt] = Mma<T>::mma(o.x[ks], frag_rowk(sHl[hb], LDH, 16 * nt, ks * KW), acc_o[nt]);
+        }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc_o[nt] *= o.v[NT];
+    }
+    __syncthreads();  // Delta^T complete; all readers of the other h^T buffer are done
+    if (!orole) {
+      // h <- e^{gamma_L} h + K^T (E Delta)
 #pragma unroll
       for (int mt = 0; mt < MTH; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) store_acc4(hb + acc_off(dkw / 16 + mt, dv0 / 16 + nt, DV), acc_h[mt][nt]);
-    }
-    __syncthreads();  // h^T in LDS is complete; last chunk's readers of Delta are done
-    // W h and (MODE 2) Q h, rows 16w
-    f32x4 acc_d[NT], acc_o[NT];
+        for (int nt = 0; nt < NT; ++nt) acc_h[mt][nt] *= o.s;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc_d[nt] = acc_o[nt] = zero4();
+      for (int ks = 0; ks < KS64; ++ks)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+        for (int nt = 0; nt < NT; ++nt) {
+          const frag be = frag_rowk(sDE, LDD, 16 * nt, ks * KW);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const frag bh = frag_rowk(sH, LDH, 16 * nt, ks * KW);
-        acc_d[nt] = Mma<T>::mma(o.wf[ks], bh, acc_d[nt]);
-        if constexpr (OUT) acc_o[nt] = Mma<T>::mma(o.qf[ks], bh, acc_o[nt]);
-        if constexpr (SPLIT) {
-          const frag bl = frag_rowk(sHl, LDH, 16 * nt, ks * KW);
-          acc_d[nt] = Mma<T>::mma(o.wf[ks], bl, acc_d[nt]);
-          if constexpr (OUT) acc_o[nt] = Mma<T>::mma(o.qf[ks], bl, acc_o[nt]);
-        }
-      }
-    // Delta = U - W h; the output takes e^gamma (Q h)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc_d[nt][i] = (mtile ? 0.f : o.u[nt][i]) - acc_d[nt][i];
-      store_acc_t2(sDE, sDEl, LDD, rw, 16 * nt, acc_d[nt] * o.ee);
-      if constexpr (OUT) {
-        store_acc_t2(sD, sDl, LDD, rw, 16 * nt, acc_d[nt]);
-        acc_o[nt] *= o.eg;
-      }
-    }
-    __syncthreads();  // Delta^T complete; all readers of h^T are done
-#pragma unroll
-    for (int mt = 0; mt < MTH; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc_h[mt][nt] *= o.eL;
-#pragma unroll
-    for (int ks = 0; ks < KS64; ++ks)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const frag be = frag_rowk(sDE, LDD, 16 * nt, ks * KW);
-#pragma unroll
-        for (int mt = 0; mt < MTH; ++mt) acc_h[mt][nt] = Mma<T>::mma(o.kf[mt][ks], be, acc_h[mt][nt]);
-        if constexpr (SPLIT) {
-          const frag bel = frag_rowk(sDEl, LDD, 16 * nt, ks * KW);
-#pragma unroll
-          for (int mt = 0; mt < MTH; ++mt) acc_h[mt][nt] = Mma<T>::mma(o.kf[mt][ks], bel, acc_h[mt][nt]);
-        }
-        if constexpr (OUT) {
-          const frag bd = frag_rowk(sD, LDD, 16 * nt, ks * KW);
-          acc_o[nt] = Mma<T>::mma(o.pf[ks], bd, acc_o[nt]);
+          for (int mt = 0; mt < MTH; ++mt) acc_h[mt][nt] = Mma<T>::mma(o.x[KS + mt * KS64 + ks], be, acc_h[mt][nt]);
           if constexpr (SPLIT) {
-            const frag bdl = frag_rowk(sDl, LDD, 16 * nt, ks * KW);
-            acc_o[nt] = Mma<T>::mma(o.pf[ks], bdl, acc_o[nt]);
-            acc_o[nt] = Mma<T>::mma(o.pl[ks], bd, acc_o[nt]);
+            const frag bel = frag_rowk(sDEl, LDD, 16 * nt, ks * KW);
+#pragma unroll
+            for (int mt = 0; mt < MTH; ++mt) acc_h[mt][nt] = Mma<T>::mma(o.x[KS + mt * KS64 + ks], bel, acc_h[mt][nt]);
           }
         }
-      }
+      const int hn = OUT ? (hb ^ 1) : 0;
 #pragma unroll
-    for (int mt = 0; mt < MTH; ++mt)
+      for (int mt = 0; mt < MTH; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) store_acc_t2(sH, sHl, LDH, dkw + 16 * mt, 16 * nt, acc_h[mt][nt]);
-    if constexpr (OUT) {
-      // each wave stages its 16 output rows in LDS and writes them back as
-      // 16-byte pieces (LDS accesses of one wave are ordered: no barrier)
+        for (int nt = 0; nt < NT; ++nt) store_acc_t2(sH[hn], sHl[hn], LDH, dkw + 16 * mt, 16 * nt, acc_h[mt][nt]);
+    } else if constexpr (OUT) {
+      // + P Delta, then write o: each output wave stages its 16 rows in LDS
+      // and writes them back as 16-byte pieces (LDS accesses of one wave are
+      // ordered: no barrier)
+#pragma unroll
+      for (int ks = 0; ks < KS64; ++ks)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const frag bd = frag_rowk(sD[hb], LDD, 16 * nt, ks * KW);
+          acc_o[nt] = Mma<T>::mma(o.x[KS + ks], bd, acc_o[nt]);
+          if constexpr (SPLIT) {
+            const frag bdl = frag_rowk(sDl[hb], LDD, 16 * nt, ks * KW);
+            acc_o[nt] = Mma<T>::mma(o.x[KS + ks], bdl, acc_o[nt]);
+            acc_o[nt] = Mma<T>::mma(o.x[KS + KS64 + ks], bd, acc_o[nt]);
+          }
+        }
       const int t0 = ts + c * CH;
       const int len = min(CH, tl - c * CH);
 #pragma unroll
@@ -624,6 +658,7 @@ __global__ __launch_bounds__(256) void k_scan_fwd(const ScanFwdArgs a) {
     for (int s = 0; s < S - 1; ++s)
       if (cb + s < nc) process(cb + s, st[s]);
   }
+  if (orole) return;
   if (MODE == 0) {
 #pragma unroll
     for (int mt = 0; mt < MTH; ++mt)
@@ -770,10 +805,11 @@ static hipError_t launch_scan_fwd_t(ScanFwdArgs a, int dvt, hipStream_t st) {
   a.ntiles = ((MODE == 0 ? DK : 0) + a.DV) / dvt;
   const int grid = 8 * ((units + 7) / 8) * a.ntiles;
   if (units == 0) return hipSuccess;
-  if (dvt == 16) hipLaunchKernelGGL((k_scan_fwd<T, HS, DK, 16, MODE>), dim3(grid), dim3(256), 0, st, a);
-  else if constexpr (sizeof(T) == 2) {
-    if (dvt == 32) hipLaunchKernelGGL((k_scan_fwd<T, HS, DK, 32, MODE>), dim3(grid), dim3(256), 0, st, a);
-    else if constexpr (DK == 64) hipLaunchKernelGGL((k_scan_fwd<T, HS, DK, 64, MODE>), dim3(grid), dim3(256), 0, st, a);
+  const int nthr = MODE == 2 ? 512 : 256;
+  if (dvt == 16) hipLaunchKernelGGL((k_scan_fwd<T, HS, DK, 16, MODE>), dim3(grid), dim3(nthr), 0, st, a);
+  else if constexpr (sizeof(T) == 2 && !(MODE == 2 && DK == 128)) {
+    if (dvt == 32) hipLaunchKernelGGL((k_scan_fwd<T, HS, DK, 32, MODE>), dim3(grid), dim3(nthr), 0, st, a);
+    else if constexpr (DK == 64 && MODE != 2) hipLaunchKernelGGL((k_scan_fwd<T, HS, DK, 64, MODE>), dim3(grid), dim3(nthr), 0, st, a);
     else return hipErrorInvalidValue;
   } else {
     return hipErrorInvalidValue;

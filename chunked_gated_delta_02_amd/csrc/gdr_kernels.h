@@ -142,26 +142,39 @@ struct GradArgs {
 // before its first LDS store (compile-time trip count), so their latencies
 // overlap instead of adding up.
 template <typename T, int NC, int NR = 64>
-__device__ __forceinline__ void load_rows(T* s, int ld, const T* g, int64_t gstride, int nvalid) {
-  constexpr int VEC = 16 / sizeof(T);
-  constexpr int PER_ROW = NC / VEC;
-  constexpr int NP = NR * PER_ROW;
-  constexpr int IT = (NP + 255) / 256;
+struct RowBuf {
+  static constexpr int VEC = 16 / sizeof(T);
+  static constexpr int PER_ROW = NC / VEC;
+  static constexpr int NP = NR * PER_ROW;
+  static constexpr int IT = (NP + 255) / 256;
   typedef float f4 __attribute__((ext_vector_type(4)));
   f4 v[IT];
+  // issue the loads (registers only)
+  __device__ __forceinline__ void load(const T* g, int64_t gstride, int nvalid) {
 #pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int e = threadIdx.x + 256 * it;
-    const int r = e / PER_ROW, c = (e - r * PER_ROW) * VEC;
-    v[it] = (f4){0.f, 0.f, 0.f, 0.f};
-    if (e < NP && r < nvalid) v[it] = *reinterpret_cast<const f4*>(g + r * gstride + c);
+    for (int it = 0; it < IT; ++it) {
+      const int e = threadIdx.x + 256 * it;
+      const int r = e / PER_ROW, c = (e - r * PER_ROW) * VEC;
+      v[it] = (f4){0.f, 0.f, 0.f, 0.f};
+      if (e < NP && r < nvalid) v[it] = *reinterpret_cast<const f4*>(g + r * gstride + c);
+    }
   }
+  // write them to LDS
+  __device__ __forceinline__ void store(T* s, int ld) const {
 #pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int e = threadIdx.x + 256 * it;
-    const int r = e / PER_ROW, c = (e - r * PER_ROW) * VEC;
-    if (e < NP) *reinterpret_cast<f4*>(s + r * ld + c) = v[it];
+    for (int it = 0; it < IT; ++it) {
+      const int e = threadIdx.x + 256 * it;
+      const int r = e / PER_ROW, c = (e - r * PER_ROW) * VEC;
+      if (e < NP) *reinterpret_cast<f4*>(s + r * ld + c) = v[it];
+    }
   }
+};
+
+template <typename T, int NC, int NR = 64>
+__device__ __forceinline__ void load_rows(T* s, int ld, const T* g, int64_t gstride, int nvalid) {
+  RowBuf<T, NC, NR> b;
+  b.load(g, gstride, nvalid);
+  b.store(s, ld);
 }
 
 template <typename T>
