@@ -146,18 +146,14 @@ gdr::Geo make_geo(const gdr_problem* p, const Plan& pl, const int32_t* cu, char*
 
 // Column tile of the serial scans.  A wider tile reads each chunk operand
 // once for more columns, a narrower one gives more workgroups: take the
-// widest that still gives one workgroup per compute unit (256 in all; the
-// scans run one or two per CU), among the tiles that fit in registers
-// without spilling (64 only with DK = 64).  The fp32 path always uses 16
-// (its operand fragments are 8x larger per k).
-// The output scan (8 waves, two roles) fits in registers only up to
-// 32 columns at DK = 64 and 16 at DK = 128.
+// widest that still gives one workgroup per compute unit (256 in all), among
+// the tiles that fit in registers without spilling (32 at most; the output
+// scan 16 with DK = 128).  The fp32 path always uses 16 (its operand
+// fragments are 8x larger per k).
 int pick_dvt(long units, int cols, bool f32, int dk, bool out = false) {
   if (f32) return 16;
-  if (out) return (dk == 64 && units * (cols / 32) >= 256) ? 32 : 16;
-  if (dk == 64 && units * (cols / 64) >= 256) return 64;
-  if (units * (cols / 32) >= 256) return 32;
-  return 16;
+  if (out && dk == 128) return 16;
+  return units * (cols / 32) >= 256 ? 32 : 16;
 }
 
 char* align_ws(void* ws) { return (char*)(((uintptr_t)ws + 255) & ~(uintptr_t)255); }

@@ -264,7 +264,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
   constexpr int PH2 = (2 * 64 * LDK + DK * L64 + 64 * L64) * (int)sizeof(T);
   extern __shared__ __align__(16) char smem[];
   T* sT = (T*)smem;                       // T (r, s), operand copy
-  float* sg = (float*)(sT + 64 * L64);    // gamma
+  float* sg = (float*)(sT + 64 * L64);    // gamma * log2(e)
   float* sb = sg + 64;                    // beta
   float* seg = sb + 64;                   // e^gamma
   float* sE = seg + 64;                   // e^{gamma_L - gamma}
@@ -298,7 +298,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
   const float scale = a.scale;
 
   if (tid < 64) {
-    sg[tid] = a.gam[ch * GSTRIDE + tid];
+    sg[tid] = a.gam[ch * GSTRIDE + tid] * LOG2E;
     sb[tid] = (tid < len) ? a.beta[(int64_t)(t0 + tid) * H + h] : 0.f;
     seg[tid] = a.gam[ch * GSTRIDE + 64 + tid];
     sE[tid] = a.gam[ch * GSTRIDE + 128 + tid];
@@ -479,7 +479,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
       const int r = r0 + i, s = 16 * nt + acc_col();
       const float dp = (s <= r) ? scale * aP[nt][i] : 0.f;
       aP[nt][i] = dp;
-      dq4[i] = (s <= r) ? dp * expf(sg[r] - sg[s]) : 0.f;
+      dq4[i] = (s <= r) ? dp * exp2_hw(sg[r] - sg[s]) : 0.f;
     }
     store_acc_t(sdQKT, L64, rw, 16 * nt, dq4);
   }
@@ -502,7 +502,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = r0 + i, s = 16 * nt + acc_col();
-        const float x = (s <= r) ? aP[nt][i] * aPP[nt][i] * expf(sg[r] - sg[s]) : 0.f;
+        const float x = (s <= r) ? aP[nt][i] * aPP[nt][i] * exp2_hw(sg[r] - sg[s]) : 0.f;
         rg[i] += x;
         cs += x;
       }
@@ -650,7 +650,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
         const int r = r0 + i, s = 16 * nt + acc_col();
         float gv = 0.f;
         if (s < r) {
-          const float Gm = expf(sg[r] - sg[s]);
+          const float Gm = exp2_hw(sg[r] - sg[s]);
           const float dA = -aA[nt][i];
           rb[i] += dA * aKK[nt][i] * Gm;
           const float X = dA * sb[r] * aKK[nt][i] * Gm;
@@ -722,7 +722,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
                   sRed[1 * 256 + 3 * 64 + l]);
     if (l == 63) {
       // gamma_L terms: e^{gamma_L} <dh, h> and sum_r E_r rowsum(K * Delta dh^T)
-      dgam += expf(sg[63]) * (sMisc[0] + sMisc[1] + sMisc[2] + sMisc[3]) +
+      dgam += exp2_hw(sg[63]) * (sMisc[0] + sMisc[1] + sMisc[2] + sMisc[3]) +
               (sMisc[4] + sMisc[5] + sMisc[6] + sMisc[7]);
     }
     const float dgv = wave_suffix_scan(dgam);
@@ -743,7 +743,6 @@ static hipError_t launch_scan_bwd_t(ScanBwdArgs a, int dvt, hipStream_t st) {
   if (dvt == 16) hipLaunchKernelGGL((k_scan_bwd<T, DK, 16, MODE>), dim3(grid), dim3(256), 0, st, a);
   else if constexpr (sizeof(T) == 2) {
     if (dvt == 32) hipLaunchKernelGGL((k_scan_bwd<T, DK, 32, MODE>), dim3(grid), dim3(256), 0, st, a);
-    else if constexpr (DK == 64) hipLaunchKernelGGL((k_scan_bwd<T, DK, 64, MODE>), dim3(grid), dim3(256), 0, st, a);
     else return hipErrorInvalidValue;
   } else {
     return hipErrorInvalidValue;

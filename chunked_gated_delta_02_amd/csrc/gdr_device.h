@@ -275,6 +275,14 @@ __device__ __forceinline__ void store_acc(T* dst, int64_t ld, int r0, int c0, f3
 }
 
 // ---------------------------------------------------------------------------
+// Gate factors.  Kernels keep gamma in LDS pre-multiplied by log2(e), so a
+// factor exp(gamma_r - gamma_s) is one hardware 2^x (v_exp_f32) of a
+// difference; the extra rounding (about |gamma| * 2^-24 relative) is of the
+// order of the cumulative sum's own.
+constexpr float LOG2E = 1.4426950408889634f;
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
 // Wavefront scans over 64 lanes.
 __device__ __forceinline__ float wave_incl_scan(float x) {
   const int l = lane_id();

@@ -144,7 +144,7 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
     const float gm = wave_incl_scan(gv);
     const float gL = __shfl(gm, 63, 64);
     const float eg = expf(gm), eE = expf(gL - gm);
-    sg[l] = gm;
+    sg[l] = gm * LOG2E;
     sb[l] = bv;
     seg[l] = eg;
     sE[l] = eE;
@@ -177,7 +177,7 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * w + acc_row0() + i, s = 16 * nt + acc_col();
-        sA[r * LDF + s] = (s < r) ? sb[r] * acc[nt][i] * expf(sg[r] - sg[s]) : 0.f;
+        sA[r * LDF + s] = (s < r) ? sb[r] * acc[nt][i] * exp2_hw(sg[r] - sg[s]) : 0.f;
       }
   }
   __syncthreads();
@@ -333,7 +333,7 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int x = 16 * w + acc_row0() + i, y = 16 * nt + acc_col();
         const int r = BWD ? y : x, s = BWD ? x : y;
-        acc[nt][i] = (s <= r) ? acc[nt][i] * expf(sg[r] - sg[s]) : 0.f;
+        acc[nt][i] = (s <= r) ? acc[nt][i] * exp2_hw(sg[r] - sg[s]) : 0.f;
       }
       store_acc(sPT, LDF, 16 * w, 16 * nt, acc[nt]);
     }
@@ -809,7 +809,6 @@ static hipError_t launch_scan_fwd_t(ScanFwdArgs a, int dvt, hipStream_t st) {
   if (dvt == 16) hipLaunchKernelGGL((k_scan_fwd<T, HS, DK, 16, MODE>), dim3(grid), dim3(nthr), 0, st, a);
   else if constexpr (sizeof(T) == 2 && !(MODE == 2 && DK == 128)) {
     if (dvt == 32) hipLaunchKernelGGL((k_scan_fwd<T, HS, DK, 32, MODE>), dim3(grid), dim3(nthr), 0, st, a);
-    else if constexpr (DK == 64 && MODE != 2) hipLaunchKernelGGL((k_scan_fwd<T, HS, DK, 64, MODE>), dim3(grid), dim3(nthr), 0, st, a);
     else return hipErrorInvalidValue;
   } else {
     return hipErrorInvalidValue;

@@ -11,6 +11,7 @@
 // e^{gamma_L - gamma}[64]
 #define GSTRIDE 192
 
+
 namespace gdr {
 
 // LDS row padding in elements: 16 bytes for 16-bit tiles (keeps 16-byte
