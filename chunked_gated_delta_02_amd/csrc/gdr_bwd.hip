@@ -356,11 +356,12 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
       t4 gv[IH], dv4[ID];   // dh snapshot and dDelta, io dtype
       {
         const float* Ub = a.Ua + ch * 64 * DV;
+        const __amdgpu_buffer_rsrc_t rdo = buf_rsrc(dop + rowq * DV + dvb, len * H * DV * (int)sizeof(T));
 #pragma unroll
         for (int nt = 0; nt < NTB; ++nt) aD[nt] = load4f(Ub + acc_off(w, dvb / 16 + nt, DV));
 #pragma unroll
         for (int ks = 0; ks < DVB / KW; ++ks)
-          dof[ks] = frag_rowk_masked(dop + rowq * DV + dvb, (int64_t)H * DV, rw, ks * KW, len);
+          dof[ks] = frag_rowk_buf<T>(rdo, H * DV, rw, ks * KW);
       }
 #pragma unroll
       for (int q = 0; q < IH; ++q) {
@@ -450,16 +451,20 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
 #pragma unroll
         for (int nt = 0; nt < NTB; ++nt) aVb[nt] = Mma<T>::mma(at, frag_rowk(sDDt, L64, 16 * nt, ks), aVb[nt]);
       }
-      T* dvp = (T*)a.dv;
+      const __amdgpu_buffer_rsrc_t rdv = buf_rsrc((T*)a.dv + rowq * DV + dvb, len * H * DV * (int)sizeof(T));
+      const AccRows arv = acc_rows(H * DV, rw, (int)sizeof(T));
 #pragma unroll
-      for (int nt = 0; nt < NTB; ++nt)
+      for (int nt = 0; nt < NTB; ++nt) {
+        f32x4 y;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int s = r0 + i, dvl = 16 * nt + acc_col();
           const float x = aVb[nt][i];
           rb[i] += to_f32(sV[s * LDV + dvl]) * x;
-          if (s < len) dvp[((int64_t)(t0 + s) * H + h) * DV + dvb + dvl] = from_f32<T>(sb[s] * x);
+          y[i] = sb[s] * x;
         }
+        buf_store_acc<T>(rdv, arv, 16 * nt, y);
+      }
     }
   }
 
@@ -527,14 +532,10 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
 #pragma unroll
       for (int nt = 0; nt < NTK; ++nt) aQ[nt] = Mma<T>::mma(af, frag_colk_lds(sK, LDK, 16 * nt, ks), aQ[nt]);
     }
-    T* dqp = (T*)a.dq;
+    const __amdgpu_buffer_rsrc_t rdq = buf_rsrc((T*)a.dq + rowq * DK, len * H * DK * (int)sizeof(T));
+    const AccRows ark = acc_rows(H * DK, rw, (int)sizeof(T));
 #pragma unroll
-    for (int nt = 0; nt < NTK; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = r0 + i;
-        if (r < len) dqp[((int64_t)(t0 + r) * H + h) * DK + 16 * nt + acc_col()] = from_f32<T>(aQ[nt][i]);
-      }
+    for (int nt = 0; nt < NTK; ++nt) buf_store_acc<T>(rdq, ark, 16 * nt, aQ[nt]);
   }
   // dk = E (Delta dh^T) + (dP * Gam)^T Q ; dgamma -= y, gamma_L += sum y
   {
@@ -689,14 +690,10 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
         aKt[nt] = Mma<T>::mma(a2, bk, aKt[nt]);
       }
     }
-    T* dkp = (T*)a.dk;
+    const __amdgpu_buffer_rsrc_t rdk = buf_rsrc((T*)a.dk + rowq * DK, len * H * DK * (int)sizeof(T));
+    const AccRows ark = acc_rows(H * DK, rw, (int)sizeof(T));
 #pragma unroll
-    for (int nt = 0; nt < NTK; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = r0 + i;
-        if (r < len) dkp[((int64_t)(t0 + r) * H + h) * DK + 16 * nt + acc_col()] = from_f32<T>(aKt[nt][i]);
-      }
+    for (int nt = 0; nt < NTK; ++nt) buf_store_acc<T>(rdk, ark, 16 * nt, aKt[nt]);
   }
   // row sums -> LDS (one writer per row), then dbeta, dgamma -> dg
 #pragma unroll

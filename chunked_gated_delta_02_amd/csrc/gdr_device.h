@@ -105,6 +105,45 @@ __device__ __forceinline__ typename Mma<T>::frag frag_rowk_masked(const T* p, in
   }
 }
 
+// Raw buffer resource over the bytes [p, p + bytes).  The hardware range
+// check of raw buffers (stride 0) makes loads past the end return zero and
+// drops stores past it, so a chunk's rows beyond its length need no branch:
+// with p at the chunk's first row and bytes = length x row stride, exactly
+// the rows past the length fall outside.  Offsets are 32-bit byte offsets.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
+}
+
+// RowK fragment from a buffer (element offsets; ld = row stride in elements)
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag frag_rowk_buf(__amdgpu_buffer_rsrc_t r, int ld, int i0, int k0) {
+  const int l = lane_id();
+  const int off = ((i0 + (l & 15)) * ld + k0 + Mma<T>::KPL * (l >> 4)) * (int)sizeof(T);
+  if constexpr (Mma<T>::KPL == 8) {
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  } else {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+  }
+}
+
+// 16 bytes from a buffer at byte offset off
+__device__ __forceinline__ f32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// One element of type T to a buffer at byte offset voff + soff.  The row
+// part of an offset must be in voff, the per-lane offset: it decides the
+// range check (soff, a uniform offset inside the row, cannot move a store
+// across a row boundary).
+template <typename T>
+__device__ __forceinline__ void buf_store1(__amdgpu_buffer_rsrc_t r, float x, int voff, int soff) {
+  if constexpr (sizeof(T) == 2) {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, from_f32<T>(x)), r, voff, soff, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), r, voff, soff, 0);
+  }
+}
+
 // ColK from LDS.  bf16 uses the gfx950 transposing LDS read
 // ds_read_b64_tr_b16: within each 16-lane group, lane j addresses the 4
 // contiguous elements at (row j>>2, cols 4*(j&3)..+3) of a 4 x 16 block and
@@ -162,6 +201,28 @@ __device__ __forceinline__ int64_t acc_off_l(int m, int n, int C, int l) {
 // r0 = 4*(l>>4), c = l & 15 (relative to the tile origin).
 __device__ __forceinline__ int acc_row0() { return 4 * (lane_id() >> 4); }
 __device__ __forceinline__ int acc_col() { return lane_id() & 15; }
+
+// Byte offsets of the lane's 4 accumulator rows (rows r0 + acc_row0() + i,
+// column acc_col()) in a buffer of rows with stride ld elements of size sz
+struct AccRows {
+  int off[4];
+};
+__device__ __forceinline__ AccRows acc_rows(int ld, int r0, int sz) {
+  AccRows a;
+  const int o = ((r0 + acc_row0()) * ld + acc_col()) * sz;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a.off[i] = o + i * ld * sz;
+  return a;
+}
+
+// An accumulator tile to the buffer rows of ar, starting at column c0 (the
+// column offset goes in the uniform offset)
+template <typename T>
+__device__ __forceinline__ void buf_store_acc(__amdgpu_buffer_rsrc_t r, const AccRows& ar, int c0, f32x4 v) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) buf_store1<T>(r, v[i], ar.off[i], c0 * (int)sizeof(T));
+}
+
 
 // Store an accumulator tile transposed: dst[(c0 + c) * ld + (r0 + r0l + i)],
 // i.e. the 4 consecutive rows of the lane become 4 contiguous elements.

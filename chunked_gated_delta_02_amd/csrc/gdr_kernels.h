@@ -137,43 +137,45 @@ struct GradArgs {
 };
 
 // ---------------------------------------------------------------------------
-// LDS staging (workgroups of 256 threads).  NR rows of NC elements from
+// LDS staging (workgroups of NTHR threads, 256 unless stated).  NR rows of NC elements from
 // global (row stride gstride elements) into LDS (row stride ld); rows >=
 // nvalid are zero.  16-byte accesses.  All of a thread's loads are issued
 // before its first LDS store (compile-time trip count), so their latencies
 // overlap instead of adding up.
-template <typename T, int NC, int NR = 64>
+template <typename T, int NC, int NR = 64, int NTHR = 256>
 struct RowBuf {
   static constexpr int VEC = 16 / sizeof(T);
   static constexpr int PER_ROW = NC / VEC;
   static constexpr int NP = NR * PER_ROW;
-  static constexpr int IT = (NP + 255) / 256;
+  static constexpr int IT = (NP + NTHR - 1) / NTHR;
   typedef float f4 __attribute__((ext_vector_type(4)));
   f4 v[IT];
-  // issue the loads (registers only)
+  // issue the loads (registers only); rows >= nvalid read as zero through
+  // the buffer range check
   __device__ __forceinline__ void load(const T* g, int64_t gstride, int nvalid) {
+    static_assert(NP % NTHR == 0, "whole trips only");
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(g, nvalid * (int)gstride * (int)sizeof(T));
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      const int e = threadIdx.x + 256 * it;
+      const int e = threadIdx.x + NTHR * it;
       const int r = e / PER_ROW, c = (e - r * PER_ROW) * VEC;
-      v[it] = (f4){0.f, 0.f, 0.f, 0.f};
-      if (e < NP && r < nvalid) v[it] = *reinterpret_cast<const f4*>(g + r * gstride + c);
+      v[it] = buf_load16(rs, (r * (int)gstride + c) * (int)sizeof(T));
     }
   }
   // write them to LDS
   __device__ __forceinline__ void store(T* s, int ld) const {
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      const int e = threadIdx.x + 256 * it;
+      const int e = threadIdx.x + NTHR * it;
       const int r = e / PER_ROW, c = (e - r * PER_ROW) * VEC;
       if (e < NP) *reinterpret_cast<f4*>(s + r * ld + c) = v[it];
     }
   }
 };
 
-template <typename T, int NC, int NR = 64>
+template <typename T, int NC, int NR = 64, int NTHR = 256>
 __device__ __forceinline__ void load_rows(T* s, int ld, const T* g, int64_t gstride, int nvalid) {
-  RowBuf<T, NC, NR> b;
+  RowBuf<T, NC, NR, NTHR> b;
   b.load(g, gstride, nvalid);
   b.store(s, ld);
 }
