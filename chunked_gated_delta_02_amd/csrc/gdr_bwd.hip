@@ -460,9 +460,11 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
         for (int i = 0; i < 4; ++i) {
           const int s = r0 + i, dvl = 16 * nt + acc_col();
           const float x = aVb[nt][i];
-          rb[i] += to_f32(sV[s * LDV + dvl]) * x;
           y[i] = sb[s] * x;
         }
+        const auto vv = lds_acc(sV, LDV, rw, 16 * nt);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rb[i] += vv[i] * aVb[nt][i];
         buf_store_acc<T>(rdv, arv, 16 * nt, y);
       }
     }
@@ -475,16 +477,23 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
   // dW^T -> LDS (aW holds dW rows 16w)
 #pragma unroll
   for (int nt = 0; nt < NTK; ++nt) store_acc_t(sdWT, L64, rw, 16 * nt, aW[nt]);
+  // gate factor of the 64-wide products at (row r0 + i, column 16 nt +
+  // acc_col()): Gam = e^{gamma_r - gamma_s} for s <= r, else 0; per-row and
+  // per-column gate values are read from LDS where they are used
+  auto gam = [&](int nt, int i) {
+    const int r = r0 + i, s = 16 * nt + acc_col();
+    const float e = exp2_hw(sg[r] - sg[s]);
+    return (s <= r) ? e : 0.f;
+  };
   // dP (scaled, masked) and dQK = dP * Gam -> LDS as (dP * Gam)^T
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
     f32x4 dq4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = r0 + i, s = 16 * nt + acc_col();
-      const float dp = (s <= r) ? scale * aP[nt][i] : 0.f;
+      const float dp = (16 * nt + acc_col() <= r0 + i) ? scale * aP[nt][i] : 0.f;
       aP[nt][i] = dp;
-      dq4[i] = (s <= r) ? dp * exp2_hw(sg[r] - sg[s]) : 0.f;
+      dq4[i] = dp * gam(nt, i);
     }
     store_acc_t(sdQKT, L64, rw, 16 * nt, dq4);
   }
@@ -506,8 +515,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
       float cs = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = r0 + i, s = 16 * nt + acc_col();
-        const float x = (s <= r) ? aP[nt][i] * aPP[nt][i] * exp2_hw(sg[r] - sg[s]) : 0.f;
+        const float x = aP[nt][i] * aPP[nt][i] * gam(nt, i);
         rg[i] += x;
         cs += x;
       }
@@ -518,14 +526,15 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
   // dq = e^gamma (scale dO h^T) + (dP * Gam) K ; dgamma += e^gamma rowsum(Q * scale dO h^T)
   {
 #pragma unroll
-    for (int nt = 0; nt < NTK; ++nt)
+    for (int nt = 0; nt < NTK; ++nt) {
+      const auto qv = lds_acc(sQ, LDK, rw, 16 * nt);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = r0 + i, dk = 16 * nt + acc_col();
-        const float x = scale * aQ[nt][i];
-        rg[i] += seg[r] * x * to_f32(sQ[r * LDK + dk]);
-        aQ[nt][i] = seg[r] * x;
+        const float x = seg[r0 + i] * scale * aQ[nt][i];
+        rg[i] += x * qv[i];
+        aQ[nt][i] = x;
       }
+    }
 #pragma unroll
     for (int ks = 0; ks < 64; ks += KW) {
       const frag af = frag_colk_lds(sdQKT, L64, rw, ks);
@@ -540,15 +549,16 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
   // dk = E (Delta dh^T) + (dP * Gam)^T Q ; dgamma -= y, gamma_L += sum y
   {
 #pragma unroll
-    for (int nt = 0; nt < NTK; ++nt)
+    for (int nt = 0; nt < NTK; ++nt) {
+      const auto kv = lds_acc(sK, LDK, rw, 16 * nt);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = r0 + i, dk = 16 * nt + acc_col();
-        const float y = sE[r] * aKt[nt][i] * to_f32(sK[r * LDK + dk]);
+        aKt[nt][i] *= sE[r0 + i];
+        const float y = aKt[nt][i] * kv[i];
         rg[i] -= y;
         gLy += y;
-        aKt[nt][i] *= sE[r];
       }
+    }
 #pragma unroll
     for (int ks = 0; ks < 64; ks += KW) {
       const frag af = frag_rowk(sdQKT, L64, rw, ks);
@@ -569,13 +579,14 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
     }
     float sr[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int nt = 0; nt < NTK; ++nt)
+    for (int nt = 0; nt < NTK; ++nt) {
+      const auto kv = lds_acc(sK, LDK, rw, 16 * nt);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = r0 + i, dk = 16 * nt + acc_col();
-        sr[i] += to_f32(sK[r * LDK + dk]) * aKb[nt][i];
-        aKt[nt][i] += sb[r] * seg[r] * aKb[nt][i];
+        sr[i] += kv[i] * aKb[nt][i];
+        aKt[nt][i] += sb[r0 + i] * seg[r0 + i] * aKb[nt][i];
       }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = r0 + i;
@@ -648,6 +659,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
       float cs = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        // strictly lower part: Gam without its diagonal
         const int r = r0 + i, s = 16 * nt + acc_col();
         float gv = 0.f;
         if (s < r) {

@@ -169,6 +169,43 @@ __device__ __forceinline__ typename Mma<T>::frag frag_colk_lds(const T* p, int l
   }
 }
 
+// The lane's accumulator-layout elements (rows r0 + acc_row0() + i, column
+// c0 + acc_col()) of a row-major LDS tile.  16-bit tiles take one
+// transposing read per 16 x 16 tile: 16-lane group g reads the 4 x 16 block
+// at rows r0 + 4g, lane j addressing (row j>>2, cols 4(j&3)..+3), and lane j
+// receives column j of the block -- its 4 accumulator rows.  The values stay
+// in the tile's type until read (operator[] converts to fp32).  Requires
+// ld % 4 == 0 and c0 % 4 == 0.
+template <typename T> struct AccVals {
+  i16x4 v;
+  // the whole vector is reinterpreted at once: a bit cast of a single
+  // element of a short vector to a 16-bit float type is miscompiled here
+  // (every element then reads element 0)
+  __device__ __forceinline__ float operator[](int i) const {
+    typedef T t4 __attribute__((ext_vector_type(4)));
+    return to_f32(__builtin_bit_cast(t4, v)[i]);
+  }
+};
+template <> struct AccVals<float> {
+  f32x4 v;
+  __device__ __forceinline__ float operator[](int i) const { return v[i]; }
+};
+template <typename T>
+__device__ __forceinline__ AccVals<T> lds_acc(const T* p, int ld, int r0, int c0) {
+  const int l = lane_id();
+  AccVals<T> r;
+  if constexpr (sizeof(T) == 2) {
+    const int j = l & 15;
+    const GDR_LDS i16x4* a0 =
+        (const GDR_LDS i16x4*)((const GDR_LDS T*)p + (r0 + 4 * (l >> 4) + (j >> 2)) * ld + c0 + 4 * (j & 3));
+    r.v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GDR_LDS i16x4*)a0);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.v[i] = p[(r0 + 4 * (l >> 4) + i) * ld + c0 + (l & 15)];
+  }
+  return r;
+}
+
 // ---------------------------------------------------------------------------
 // Fragment order ("afrag"): an R x K operand matrix (rows i, contraction
 // index k) stored so that the fragment of row tile m and k-step s -- what
