@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--h-store", choices=("f32", "f16", "bf16"), default=None,
                     help="snapshot dtype (default: the workload's)")
+    ap.add_argument("--recompute", action="store_true",
+                    help="the forward keeps no state snapshots and the backward recomputes them "
+                         "(default: the forward saves them for the backward)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the oracle sample")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -318,12 +321,13 @@ def main():
     o = torch.empty_like(v)
     hT = torch.empty(sshape, dtype=torch.float32, device=dev)
     hs_dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.h_store]
-    h_saved = torch.empty(_lib.gdr_h_saved_bytes(p) // hs_dt.itemsize, dtype=hs_dt, device=dev)
+    h_saved = None if args.recompute else \
+        torch.empty(_lib.gdr_h_saved_bytes(p) // hs_dt.itemsize, dtype=hs_dt, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dbeta, dg = torch.empty_like(beta), torch.empty_like(g)
     dh0 = torch.empty(sshape, dtype=torch.float32, device=dev)
     fws = _lib.gdr_fwd_workspace_bytes(p)
-    bws = _lib.gdr_bwd_workspace_bytes(p, True)
+    bws = _lib.gdr_bwd_workspace_bytes(p, h_saved is not None)
     wsf = torch.empty(fws, dtype=torch.uint8, device=dev)
     wsb = torch.empty(bws, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
@@ -443,6 +447,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "T": T, "H": H, "DK": K, "DV": V, "chunk": CH,
                    "layout": w.layout, "h_store": w.h_store, "cp_segments": w.cp_segments, "seed": w.seed,
+                   "snapshots": "recomputed" if args.recompute else "saved",
                    "parallelism": "single GPU"},
         "tflops": {"fwd+bwd": round((fl_f + fl_b) / (ms_step * 1e-3) / 1e12, 2),
                    "fwd_kernels": round(fl_f / (fwd_ms * 1e-3) / 1e12, 2) if fwd_ms else None,

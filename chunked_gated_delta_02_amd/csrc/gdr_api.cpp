@@ -188,7 +188,7 @@ gdr_status gdr_check(const gdr_problem* p) {
 
 size_t gdr_fwd_workspace_bytes(const gdr_problem* p) {
   if (check_problem(p) != GDR_OK) return 0;
-  return make_plan(p, 0, true).total;
+  return make_plan(p, 0, false).total;
 }
 
 size_t gdr_bwd_workspace_bytes(const gdr_problem* p, int have_h_saved) {
@@ -215,7 +215,7 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, con
   const void* ptrs[] = {q, k, v, beta, g, o, h0, hT, h_saved, cu_seqlens};
   for (const void* ptr : ptrs)
     if (ptr && misaligned(ptr)) { set_err("all buffers must be 16-byte aligned"); return GDR_ERR_INVALID_ARG; }
-  const Plan pl = make_plan(p, 0, h_saved == nullptr);
+  const Plan pl = make_plan(p, 0, false);   // snapshots go to h_saved or nowhere
   if (!workspace || workspace_bytes < pl.total) {
     set_err("workspace of %zu bytes needed (got %zu)", pl.total, workspace ? workspace_bytes : (size_t)0);
     return GDR_ERR_WORKSPACE;
@@ -224,7 +224,7 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, con
   hipStream_t s = (hipStream_t)stream;
   const float scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->dk);
   gdr::Geo geo = make_geo(p, pl, cu_seqlens, ws);
-  void* hs = h_saved ? h_saved : (void*)(ws + pl.hs);
+  void* hs = h_saved;
 
   if (p->varlen)
     GDR_LAUNCH(GDR_KERNEL_PLAN, s, gdr::launch_plan(cu_seqlens, pl.N, p->seqlen, pl.NCb, (int*)(ws + pl.seq_chunk), (int*)(ws + pl.chunk_seq), s));
@@ -247,7 +247,8 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, con
     gdr::CpChainArgs ca{geo, p->dk, p->dv, p->layout, 0, h0, (const float*)(ws + pl.summ), (float*)(ws + pl.hst)};
     GDR_LAUNCH(GDR_KERNEL_CP_CHAIN_FWD, s, gdr::launch_cp_chain(ca, s));
   }
-  GDR_LAUNCH(GDR_KERNEL_SCAN_FWD, s, gdr::launch_scan_fwd(sa, pl.f32, p->h_store_dtype, p->dk, pick_dvt(units, p->dv, pl.f32, p->dk, true), 2, s));
+  // mode 2 writes the snapshots to h_saved; mode 3 keeps none
+  GDR_LAUNCH(GDR_KERNEL_SCAN_FWD, s, gdr::launch_scan_fwd(sa, pl.f32, p->h_store_dtype, p->dk, pick_dvt(units, p->dv, pl.f32, p->dk, true), h_saved ? 2 : 3, s));
   return GDR_OK;
 }
 
@@ -260,8 +261,8 @@ gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, con
   gdr_status st = check_problem(p);
   if (st != GDR_OK) return st;
   const bool tokens = (int64_t)p->batch * p->seqlen > 0;
-  if (tokens && (!q || !k || !v || !beta || !g || !dO || !dq || !dk || !dv || !dbeta || !dg)) {
-    set_err("q, k, v, beta, g, dO, dq, dk, dv, dbeta and dg are required");
+  if (tokens && (!q || !k || !v || !beta || !g || !dO)) {
+    set_err("q, k, v, beta, g and dO are required");
     return GDR_ERR_INVALID_ARG;
   }
   if ((p->varlen != 0) != (cu_seqlens != nullptr)) { set_err("cu_seqlens must be given exactly when varlen is 1"); return GDR_ERR_INVALID_ARG; }

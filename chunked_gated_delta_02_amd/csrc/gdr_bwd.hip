@@ -245,6 +245,8 @@ __global__ __launch_bounds__(256) void k_scan_bwd(const ScanBwdArgs a) {
 // k_grad: per (chunk, head).  Phase 1 loops over DV in blocks of DVB and
 // accumulates the DV-contracted products (dQg, dKt, dW, dP, dT_V) in
 // registers while emitting dv; phase 2 finishes dq, dk, dbeta and dg.  Wave
+// Any of dq, dk, dv, dbeta, dg may be null: its stores are then dropped
+// (empty buffer range) or skipped; the computation is the same.  Wave
 // w owns output rows 16w..16w+15 of every 64-row product, so all row sums
 // stay inside one wavefront; column sums go through per-wave LDS partials
 // reduced in a fixed order.
@@ -451,7 +453,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
 #pragma unroll
         for (int nt = 0; nt < NTB; ++nt) aVb[nt] = Mma<T>::mma(at, frag_rowk(sDDt, L64, 16 * nt, ks), aVb[nt]);
       }
-      const __amdgpu_buffer_rsrc_t rdv = buf_rsrc((T*)a.dv + rowq * DV + dvb, len * H * DV * (int)sizeof(T));
+      const __amdgpu_buffer_rsrc_t rdv = buf_rsrc((T*)a.dv + rowq * DV + dvb, a.dv ? len * H * DV * (int)sizeof(T) : 0);
       const AccRows arv = acc_rows(H * DV, rw, (int)sizeof(T));
 #pragma unroll
       for (int nt = 0; nt < NTB; ++nt) {
@@ -541,7 +543,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
 #pragma unroll
       for (int nt = 0; nt < NTK; ++nt) aQ[nt] = Mma<T>::mma(af, frag_colk_lds(sK, LDK, 16 * nt, ks), aQ[nt]);
     }
-    const __amdgpu_buffer_rsrc_t rdq = buf_rsrc((T*)a.dq + rowq * DK, len * H * DK * (int)sizeof(T));
+    const __amdgpu_buffer_rsrc_t rdq = buf_rsrc((T*)a.dq + rowq * DK, a.dq ? len * H * DK * (int)sizeof(T) : 0);
     const AccRows ark = acc_rows(H * DK, rw, (int)sizeof(T));
 #pragma unroll
     for (int nt = 0; nt < NTK; ++nt) buf_store_acc<T>(rdq, ark, 16 * nt, aQ[nt]);
@@ -702,7 +704,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
         aKt[nt] = Mma<T>::mma(a2, bk, aKt[nt]);
       }
     }
-    const __amdgpu_buffer_rsrc_t rdk = buf_rsrc((T*)a.dk + rowq * DK, len * H * DK * (int)sizeof(T));
+    const __amdgpu_buffer_rsrc_t rdk = buf_rsrc((T*)a.dk + rowq * DK, a.dk ? len * H * DK * (int)sizeof(T) : 0);
     const AccRows ark = acc_rows(H * DK, rw, (int)sizeof(T));
 #pragma unroll
     for (int nt = 0; nt < NTK; ++nt) buf_store_acc<T>(rdk, ark, 16 * nt, aKt[nt]);
@@ -736,8 +738,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
     }
     const float dgv = wave_suffix_scan(dgam);
     if (l < len) {
-      a.dg[(int64_t)(t0 + l) * H + h] = dgv;
-      a.dbeta[(int64_t)(t0 + l) * H + h] = sRB[l];
+      if (a.dg) a.dg[(int64_t)(t0 + l) * H + h] = dgv;
+      if (a.dbeta) a.dbeta[(int64_t)(t0 + l) * H + h] = sRB[l];
     }
   }
 }

@@ -409,6 +409,7 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
 //           beside them from double-buffered copies of h^T and Delta^T, so
 //           the output is off the recurrence's critical path.  Both roles
 //           meet at the same two barriers per chunk.
+//   MODE 3: MODE 2 without the snapshots (forward calls that keep none);
 //   MODE 1: writes the snapshots only (backward recompute);
 //   MODE 0: CP segment summary -- scans the augmented state [I | 0] of width
 //           DK + DV over one segment (the identity columns take U = 0, so
@@ -419,8 +420,9 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
 #define SCAN_STAGES 3
 
 template <typename T, typename HS, int DK, int DVT, int MODE>
-__global__ __launch_bounds__(MODE == 2 ? 512 : 256) void k_scan_fwd(const ScanFwdArgs a) {
-  constexpr bool OUT = MODE == 2;
+__global__ __launch_bounds__(MODE >= 2 ? 512 : 256) void k_scan_fwd(const ScanFwdArgs a) {
+  constexpr bool OUT = MODE >= 2;
+  constexpr bool SNAP = MODE == 1 || MODE == 2;
   constexpr bool SPLIT = sizeof(T) == 2;
   constexpr int P = pad_of<T>();
   constexpr int LDH = DK + P;
@@ -531,7 +533,7 @@ __global__ __launch_bounds__(MODE == 2 ? 512 : 256) void k_scan_fwd(const ScanFw
   auto process = [&](int c, Ops& o) {
     const int64_t ch = chb + c;
     const int hb = OUT ? (c & 1) : 0;   // buffer holding h_c and Delta_c
-    if constexpr (MODE != 0) {
+    if constexpr (SNAP) {
       if (!orole) {
         HS* hsb = (HS*)a.hs + ch * DK * DV;
 #pragma unroll
@@ -805,9 +807,9 @@ static hipError_t launch_scan_fwd_t(ScanFwdArgs a, int dvt, hipStream_t st) {
   a.ntiles = ((MODE == 0 ? DK : 0) + a.DV) / dvt;
   const int grid = 8 * ((units + 7) / 8) * a.ntiles;
   if (units == 0) return hipSuccess;
-  const int nthr = MODE == 2 ? 512 : 256;
+  const int nthr = MODE >= 2 ? 512 : 256;
   if (dvt == 16) hipLaunchKernelGGL((k_scan_fwd<T, HS, DK, 16, MODE>), dim3(grid), dim3(nthr), 0, st, a);
-  else if constexpr (sizeof(T) == 2 && !(MODE == 2 && DK == 128)) {
+  else if constexpr (sizeof(T) == 2 && !(MODE >= 2 && DK == 128)) {
     if (dvt == 32) hipLaunchKernelGGL((k_scan_fwd<T, HS, DK, 32, MODE>), dim3(grid), dim3(nthr), 0, st, a);
     else return hipErrorInvalidValue;
   } else {
@@ -820,6 +822,7 @@ template <typename T, typename HS, int DK>
 static hipError_t launch_scan_fwd_m(const ScanFwdArgs& a, int dvt, int mode, hipStream_t st) {
   if (mode == 0) return launch_scan_fwd_t<T, float, DK, 0>(a, dvt, st);   // no snapshots: HS unused
   if (mode == 1) return launch_scan_fwd_t<T, HS, DK, 1>(a, dvt, st);
+  if (mode == 3) return launch_scan_fwd_t<T, float, DK, 3>(a, dvt, st);  // no snapshots: HS unused
   return launch_scan_fwd_t<T, HS, DK, 2>(a, dvt, st);
 }
 

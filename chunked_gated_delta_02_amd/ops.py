@@ -105,9 +105,13 @@ def chunk_gdr_fwd(q, k, v, beta, g, cu_seqlens=None, h0=None, layout="KV", scale
     return o, hT, h_saved
 
 
+GRADS = ("dq", "dk", "dv", "dbeta", "dg")
+
+
 def chunk_gdr_bwd(q, k, v, beta, g, do, cu_seqlens=None, h0=None, dhT=None, h_saved=None,
-                  layout="KV", scale=None, h_store="f32", need_dh0=True, cp_segments=1):
-    """Backward.  Returns dict(dq, dk, dv, dbeta, dg, dh0)."""
+                  layout="KV", scale=None, h_store="f32", need_dh0=True, cp_segments=1, need=GRADS):
+    """Backward.  Returns dict(dq, dk, dv, dbeta, dg, dh0); the gradients not
+    named in ``need`` (and dh0 unless ``need_dh0``) are None and not written."""
     _check_tensors(q, k, v, beta, g, cu_seqlens, [("h0", h0), ("do", do), ("dhT", dhT), ("h_saved", h_saved)])
     if do.shape != v.shape or do.dtype != v.dtype:
         raise ValueError("do must match v in shape and dtype")
@@ -122,11 +126,14 @@ def chunk_gdr_bwd(q, k, v, beta, g, do, cu_seqlens=None, h0=None, dhT=None, h_sa
         raise _lib.GDRError(st, _lib.last_error())
     if h_saved is not None and h_saved.numel() * h_saved.element_size() < _lib.gdr_h_saved_bytes(p):
         raise ValueError("h_saved is smaller than gdr_h_saved_bytes()")
-    dq = torch.empty_like(q)
-    dk = torch.empty_like(k)
-    dv = torch.empty_like(v)
-    dbeta = torch.empty_like(beta)
-    dg = torch.empty_like(g)
+    unknown = set(need) - set(GRADS)
+    if unknown:
+        raise ValueError("unknown gradient names %s" % sorted(unknown))
+    dq = torch.empty_like(q) if "dq" in need else None
+    dk = torch.empty_like(k) if "dk" in need else None
+    dv = torch.empty_like(v) if "dv" in need else None
+    dbeta = torch.empty_like(beta) if "dbeta" in need else None
+    dg = torch.empty_like(g) if "dg" in need else None
     dh0 = torch.empty(_state_shape(N, H, DK, DV, layout), dtype=torch.float32, device=q.device) \
         if need_dh0 else None
     ws_bytes = _lib.gdr_bwd_workspace_bytes(p, h_saved is not None)
@@ -139,15 +146,18 @@ def chunk_gdr_bwd(q, k, v, beta, g, do, cu_seqlens=None, h0=None, dhT=None, h_sa
 
 
 class ChunkGDRFunction(torch.autograd.Function):
-    """Autograd over libgdr: the forward saves the per-chunk state snapshots
-    so the backward skips the state recomputation."""
+    """Autograd over libgdr.  With ``save_states`` the forward keeps the
+    per-chunk state snapshots so the backward skips their recomputation;
+    without it (or when no input needs a gradient) it keeps none.  The
+    backward writes only the gradients autograd asks for."""
 
     @staticmethod
     def forward(ctx, q, k, v, beta, g, h0, cu_seqlens, layout, scale, h_store, output_final_state,
-                cp_fwd, cp_bwd):
+                cp_fwd, cp_bwd, save_states):
+        save = save_states and any(ctx.needs_input_grad[:6])
         o, hT, h_saved = chunk_gdr_fwd(q, k, v, beta, g, cu_seqlens=cu_seqlens, h0=h0, layout=layout,
                                        scale=scale, output_final_state=output_final_state,
-                                       save_states=True, h_store=h_store, cp_segments=cp_fwd)
+                                       save_states=save, h_store=h_store, cp_segments=cp_fwd)
         ctx.save_for_backward(q, k, v, beta, g, h0, cu_seqlens, h_saved)
         ctx.layout, ctx.scale, ctx.h_store, ctx.cp_bwd = layout, scale, h_store, cp_bwd
         ctx.has_h0 = h0 is not None
@@ -158,18 +168,23 @@ class ChunkGDRFunction(torch.autograd.Function):
     @staticmethod
     def backward(ctx, do, dhT=None):
         q, k, v, beta, g, h0, cu_seqlens, h_saved = ctx.saved_tensors
+        need = tuple(n for n, want in zip(GRADS, ctx.needs_input_grad[:5]) if want)
         r = chunk_gdr_bwd(q, k, v, beta, g, do.contiguous(), cu_seqlens=cu_seqlens, h0=h0,
                           dhT=None if dhT is None else dhT.contiguous(), h_saved=h_saved,
                           layout=ctx.layout, scale=ctx.scale, h_store=ctx.h_store,
-                          need_dh0=ctx.has_h0 and ctx.needs_input_grad[5], cp_segments=ctx.cp_bwd)
-        return (r["dq"], r["dk"], r["dv"], r["dbeta"], r["dg"], r["dh0"]) + (None,) * 7
+                          need_dh0=ctx.has_h0 and ctx.needs_input_grad[5], cp_segments=ctx.cp_bwd,
+                          need=need)
+        return (r["dq"], r["dk"], r["dv"], r["dbeta"], r["dg"], r["dh0"]) + (None,) * 8
 
 
 def chunk_gdr(q, k, v, beta, g, h0=None, cu_seqlens=None, layout="KV", scale=None,
-              output_final_state=True, h_store="f32", cp_segments=1, cp_segments_bwd=None):
+              output_final_state=True, h_store="f32", cp_segments=1, cp_segments_bwd=None,
+              save_states=True):
     """Chunked gated delta rule with autograd.  Returns o, or (o, h_T).
     ``cp_segments_bwd`` (default: ``cp_segments``) sets the backward's
-    intra-card context parallelism independently of the forward's."""
+    intra-card context parallelism independently of the forward's.
+    ``save_states=False`` keeps no state snapshots between the passes (the
+    backward recomputes them: less memory, one more scan)."""
     cp_bwd = cp_segments if cp_segments_bwd is None else cp_segments_bwd
     return ChunkGDRFunction.apply(q, k, v, beta, g, h0, cu_seqlens, layout, scale, h_store,
-                                  output_final_state, cp_segments, cp_bwd)
+                                  output_final_state, cp_segments, cp_bwd, save_states)

@@ -113,16 +113,20 @@ size_t gdr_bwd_workspace_bytes(const gdr_problem* p, int have_h_saved);
 size_t gdr_h_saved_bytes(const gdr_problem* p);
 
 /* Forward.  Writes o; writes hT if non-NULL; writes the state snapshots to
- * h_saved if non-NULL (for a later gdr_chunk_bwd).  h0 may be NULL (zeros).
- * cu_seqlens must be non-NULL exactly when p->varlen is 1. */
+ * h_saved if non-NULL (for a later gdr_chunk_bwd); with h_saved NULL no
+ * snapshot is written anywhere (a later backward recomputes them).  h0 may
+ * be NULL (zeros).  cu_seqlens must be non-NULL exactly when p->varlen is
+ * 1. */
 gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
                          const float* beta, const float* g, const int32_t* cu_seqlens,
                          const float* h0, void* o, float* hT, void* h_saved, void* workspace,
                          size_t workspace_bytes, void* stream);
 
 /* Backward: gradients of L with dL/do = dO and dL/dh_T = dhT (NULL = zero).
- * Writes dq, dk, dv, dbeta, dg, and dh0 if non-NULL.  h_saved: the snapshots
- * written by gdr_chunk_fwd for the same inputs, or NULL to recompute them. */
+ * Writes each of dq, dk, dv, dbeta, dg and dh0 that is non-NULL (a NULL
+ * gradient is not written; the others are unchanged by its absence).
+ * h_saved: the snapshots written by gdr_chunk_fwd for the same inputs, or
+ * NULL to recompute them. */
 gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, const void* v,
                          const float* beta, const float* g, const int32_t* cu_seqlens,
                          const float* h0, const void* h_saved, const void* dO, const float* dhT,

@@ -159,6 +159,9 @@ def test_workspace_sizes(lib):
     assert hs == nchunks * 16 * 128 * 128 * 4
     assert b0 - b1 >= hs
     assert f > 0 and b1 > 0
+    # the forward keeps snapshots only in the caller's h_saved: its workspace
+    # does not depend on the snapshot dtype
+    assert _lib.gdr_fwd_workspace_bytes(good(h_store_dtype=_lib.GDR_F16)) == f
     assert _lib.gdr_h_saved_bytes(good(h_store_dtype=_lib.GDR_F16)) == hs // 2
     # packed batches: chunk slots bounded by ceil(T/64) + N without reading cu_seqlens
     pv = good(varlen=1, batch=1, num_seqs=8, seqlen=1000)

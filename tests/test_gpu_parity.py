@@ -165,6 +165,57 @@ def test_autograd_matches_explicit_backward():
         assert torch.equal(leaves[n].grad, r[gname]), n
 
 
+def test_autograd_without_saved_states_and_pruned_gradients():
+    """save_states=False (the backward recomputes the snapshots) gives the
+    same gradients bit for bit; inputs that need no gradient get none, and
+    the gradients that are computed do not change."""
+    w = SMALL["cfg1_fixed_bf16_ragged"].replace(has_h0=True)
+    say("[case] autograd recompute / pruned")
+    inp = gin.generate(w)
+    dev = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    names = ("q", "k", "v", "beta", "g", "h0")
+
+    def run(save, want):
+        leaves = {n: dev[n].clone().requires_grad_(n in want) for n in names}
+        o, hT = ops.chunk_gdr(*(leaves[n] for n in names[:5]), h0=leaves["h0"], layout=w.layout,
+                              save_states=save)
+        torch.autograd.backward([o, hT], [dev["do"], dev["dhT"]])
+        torch.cuda.synchronize()
+        return o.detach(), hT.detach(), {n: leaves[n].grad for n in names}
+
+    o1, h1, g1 = run(True, names)
+    o2, h2, g2 = run(False, names)
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+    for n in names:
+        assert torch.equal(g1[n], g2[n]), n
+    for want in (("q",), ("k", "g"), ("v", "beta", "h0")):
+        _, _, g3 = run(True, want)
+        for n in names:
+            if n in want:
+                assert torch.equal(g3[n], g1[n]), (want, n)
+            else:
+                assert g3[n] is None, (want, n)
+
+
+def test_backward_writes_only_requested_gradients():
+    w = SMALL["cfg2_varlen_bf16"]
+    say("[case] partial gradient outputs %s" % w.name)
+    inp = gin.generate(w)
+    dev = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    args = [dev[n] for n in ("q", "k", "v", "beta", "g", "do")]
+    kw = dict(cu_seqlens=dev["cu_seqlens"], h0=dev["h0"], dhT=dev["dhT"], layout=w.layout)
+    full = ops.chunk_gdr_bwd(*args, **kw)
+    for need in (("dk",), ("dq", "dbeta"), ("dv", "dg")):
+        part = ops.chunk_gdr_bwd(*args, need=need, **kw)
+        for n in ops.GRADS:
+            if n in need:
+                assert torch.equal(part[n], full[n]), (need, n)
+            else:
+                assert part[n] is None
+    with pytest.raises(ValueError):
+        ops.chunk_gdr_bwd(*args, need=("dx",), **kw)
+
+
 # ---------------------------------------------------------------------------
 # intra-card context parallelism: every case against the oracle (the
 # segmented scan must reach the un-segmented result within the tolerance)
