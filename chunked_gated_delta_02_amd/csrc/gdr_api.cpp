@@ -98,8 +98,10 @@ Plan make_plan(const gdr_problem* p, int mode, bool need_hs) {
     pl.chunk_seq = take(sizeof(int) * (size_t)pl.NCb);
   }
   pl.gam = take(ch * GSTRIDE * 4);
-  pl.Wf = take(ch * 64 * DK * e);
-  pl.Ua = take(ch * 64 * DV * 4);
+  if (mode == 0 || need_hs) {   // the backward's gradient kernel needs neither
+    pl.Wf = take(ch * 64 * DK * e);
+    pl.Ua = take(ch * 64 * DV * 4);
+  }
   if (need_hs) {
     pl.hs = take(ch * DV * DK * pl.hsz);
     pl.KtTf = take(ch * DK * 64 * e);
@@ -110,7 +112,7 @@ Plan make_plan(const gdr_problem* p, int mode, bool need_hs) {
     pl.Pf = take(ch * 64 * 64 * e);
     if (!pl.f32) pl.Pfl = take(ch * 64 * 64 * e);
   } else {
-    pl.Tm = take(ch * 64 * 64 * e);
+    pl.Tm = take(ch * 64 * 64 * 4);
     pl.WTf = take(ch * DK * 64 * e);
     pl.Kf = take(ch * 64 * DK * e);
     pl.dDl = take(ch * 64 * DV * 4);
@@ -289,9 +291,12 @@ gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, con
     gdr::WyArgs wa{};
     wa.geo = geo; wa.DV = p->dv; wa.scale = scale;
     wa.q = q; wa.k = k; wa.v = v; wa.dO = dO; wa.beta = beta; wa.g = g;
-    wa.gam = (float*)(ws + pl.gam); wa.Wf = ws + pl.Wf; wa.Ua = (float*)(ws + pl.Ua);
+    wa.gam = (float*)(ws + pl.gam);
+    // W (fragment order) and U only feed the snapshot recompute
+    wa.Wf = h_saved ? nullptr : (void*)(ws + pl.Wf);
+    wa.Ua = h_saved ? nullptr : (float*)(ws + pl.Ua);
     wa.KtTf = h_saved ? nullptr : (void*)(ws + pl.KtTf);
-    wa.Tm = ws + pl.Tm; wa.WTf = ws + pl.WTf; wa.Kf = ws + pl.Kf;
+    wa.Tm = (float*)(ws + pl.Tm); wa.WTf = ws + pl.WTf; wa.Kf = ws + pl.Kf;
     wa.dDl = (float*)(ws + pl.dDl); wa.Z = (float*)(ws + pl.Z);
     GDR_LAUNCH(GDR_KERNEL_WY, s, gdr::launch_wy(wa, pl.f32, p->dk, true, s));
     if (!h_saved) {
@@ -324,7 +329,7 @@ gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, con
     gdr::GradArgs ga{};
     ga.geo = geo; ga.DV = p->dv; ga.scale = scale;
     ga.q = q; ga.k = k; ga.v = v; ga.dO = dO; ga.beta = beta;
-    ga.gam = (const float*)(ws + pl.gam); ga.Wf = ws + pl.Wf; ga.Ua = (const float*)(ws + pl.Ua); ga.Tm = ws + pl.Tm;
+    ga.gam = (const float*)(ws + pl.gam); ga.WTf = ws + pl.WTf; ga.Tm = (const float*)(ws + pl.Tm);
     ga.hs = hs; ga.dhs = ws + pl.dhs; ga.dD = ws + pl.dD;
     ga.dq = dq; ga.dk = dk; ga.dv = dv; ga.dbeta = dbeta; ga.dg = dg;
     GDR_LAUNCH(GDR_KERNEL_GRAD, s, gdr::launch_grad(ga, pl.f32, p->h_store_dtype, p->dk, s));

@@ -126,14 +126,15 @@ __global__ __launch_bounds__(256) void k_scan_bwd(const ScanBwdArgs a) {
     for (int mt = 0; mt < MTH; ++mt)
 #pragma unroll
       for (int ks = 0; ks < KS64; ++ks) o.wf[mt][ks] = frag_af<T, 64>(Wb, dkw / 16 + mt, ks);
+    // the two fp32 terms are read by this tile only: streaming loads
     const float* Db = a.dDl + ch * 64 * DV;
     const float* Zb = a.Z + ch * DK * DV;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      o.dl[nt] = *reinterpret_cast<const f32x4*>(Db + acc_off(w, dv0 / 16 + nt, DV));
+      o.dl[nt] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Db + acc_off(w, dv0 / 16 + nt, DV)));
 #pragma unroll
       for (int mt = 0; mt < MTH; ++mt)
-        o.z[mt][nt] = *reinterpret_cast<const f32x4*>(Zb + acc_off(dkw / 16 + mt, dv0 / 16 + nt, DV));
+        o.z[mt][nt] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Zb + acc_off(dkw / 16 + mt, dv0 / 16 + nt, DV)));
     }
     const float* gb = a.gam + ch * GSTRIDE;
     o.ee = *reinterpret_cast<const f32x4*>(gb + 128 + rw + acc_row0());
@@ -262,7 +263,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
   constexpr int NTK = DK / 16;
   constexpr int NTB = DVB / 16;
   typedef typename Mma<T>::frag frag;
-  constexpr int PH1 = (2 * DVB * LDK + 3 * DVB * L64 + 64 * LDV) * (int)sizeof(T);
+  constexpr int PH1 = (2 * DVB * LDK + 3 * DVB * L64 + 64 * LDV + DK * L64) * (int)sizeof(T);
   constexpr int PH2 = (2 * 64 * LDK + DK * L64 + 64 * L64) * (int)sizeof(T);
   extern __shared__ __align__(16) char smem[];
   T* sT = (T*)smem;                       // T (r, s), operand copy
@@ -280,6 +281,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
   T* sDeltaTl = sDeltaT + DVB * L64;      // lo
   T* sDDt = sDeltaTl + DVB * L64;         // dDelta^T (dv, r)
   T* sV = sDDt + DVB * L64;               // V (r, dv)
+  T* sWT = sV + 64 * LDV;                 // W^T (dk, r)
   // phase 2 (aliases phase 1)
   T* sQ = (T*)uni;                        // Q (r, dk); later dT^T (s, r)
   T* sK = sQ + 64 * LDK;                  // K (r, dk)
@@ -305,16 +307,29 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
     seg[tid] = a.gam[ch * GSTRIDE + 64 + tid];
     sE[tid] = a.gam[ch * GSTRIDE + 128 + tid];
   }
+  const float* Tg = a.Tm + ch * 4096;   // T, fp32 row-major
   {
-    // T (io dtype, row-major) -> operand copy in LDS; all loads issued first
-    typedef T t4 __attribute__((ext_vector_type(4)));
-    t4 tv[4];
+    // T -> operand copy in the io dtype in LDS; W^T from fragment order into
+    // (dk, r) rows in LDS; all loads issued first
+    constexpr int KPL = Mma<T>::KPL;
+    constexpr int WPT = (DK / 16) * (64 / KW) * 64 / 256;   // W^T fragment lanes per thread
+    f32x4 tv[4];
+    frag wv[WPT];
+    const T* Wb = (const T*)a.WTf + ch * DK * 64;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) tv[q] = *reinterpret_cast<const t4*>((const T*)a.Tm + ch * 4096 + 4 * (tid + 256 * q));
+    for (int q = 0; q < 4; ++q) tv[q] = *reinterpret_cast<const f32x4*>(Tg + 4 * (tid + 256 * q));
+#pragma unroll
+    for (int q = 0; q < WPT; ++q) wv[q] = *reinterpret_cast<const frag*>(Wb + (int64_t)(tid + 256 * q) * KPL);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = 4 * (tid + 256 * q);
-      *reinterpret_cast<t4*>(sT + (e >> 6) * L64 + (e & 63)) = tv[q];
+      store_acc4(sT + (e >> 6) * L64 + (e & 63), tv[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < WPT; ++q) {
+      const int e = tid + 256 * q, f = e >> 6, ll = e & 63;
+      const int m = f / (64 / KW), ks = f - m * (64 / KW);
+      *reinterpret_cast<frag*>(sWT + (16 * m + (ll & 15)) * L64 + ks * KW + KPL * (ll >> 4)) = wv[q];
     }
   }
   const int rw = 16 * w;            // first output row of this wave
@@ -326,13 +341,12 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
   float gLh = 0.f;                      // <dh, h> partial (times e^{gamma_L} later)
   float gLy = 0.f;                      // sum of E rowsum(K * Delta dh^T) partial
 
-  // W fragments for Delta = U - W h (rows 16w), negated
-  frag wf[DK / KW];
-  {
-    const T* Wb = (const T*)a.Wf + ch * 64 * DK;
+  // T diag(beta) (rows 16w) as a split operand of U = T diag(beta) V, read
+  // from the fp32 T once the gates are in LDS
+  __syncthreads();
+  frag tbh[64 / KW], tbl[64 / KW];
 #pragma unroll
-    for (int ks = 0; ks < DK / KW; ++ks) wf[ks] = Mma<T>::neg(frag_af<T, DK>(Wb, w, ks));
-  }
+  for (int ks = 0; ks < 64 / KW; ++ks) frag_rowk_f32<T>(Tg, 64, rw, ks * KW, [&](int s2) { return sb[s2]; }, tbh[ks], tbl[ks]);
   f32x4 aQ[NTK], aKt[NTK], aW[NTK], aP[4], aTV[4];
 #pragma unroll
   for (int nt = 0; nt < NTK; ++nt) aQ[nt] = aKt[nt] = aW[nt] = zero4();
@@ -341,7 +355,6 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
 
   const int64_t rowq = (int64_t)t0 * H + h;   // token-row index of chunk row 0
   for (int dvb = 0; dvb < DV; dvb += DVB) {
-    f32x4 aD[NTB];          // Delta block = U - W h (rows 16w), starts as U
     frag dof[DVB / KW];     // dO fragments (rows 16w, k = dv)
     __syncthreads();
     // h and dh (accumulator order <DK, DV>) and dDelta (accumulator order
@@ -357,10 +370,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
       f32x4 hv[IH];
       t4 gv[IH], dv4[ID];   // dh snapshot and dDelta, io dtype
       {
-        const float* Ub = a.Ua + ch * 64 * DV;
         const __amdgpu_buffer_rsrc_t rdo = buf_rsrc(dop + rowq * DV + dvb, len * H * DV * (int)sizeof(T));
-#pragma unroll
-        for (int nt = 0; nt < NTB; ++nt) aD[nt] = load4f(Ub + acc_off(w, dvb / 16 + nt, DV));
 #pragma unroll
         for (int ks = 0; ks < DVB / KW; ++ks)
           dof[ks] = frag_rowk_buf<T>(rdo, H * DV, rw, ks * KW);
@@ -399,15 +409,27 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
     }
     load_rows<T, DVB>(sV, LDV, vp + rowq * DV + dvb, (int64_t)H * DV, len);
     __syncthreads();
-    // Delta block = U - W h  (rows 16w)
+    // Delta block = U - W h = T diag(beta) V - W h  (rows 16w)
     {
+      f32x4 aD[NTB], aH[NTB];
 #pragma unroll
-      for (int ks = 0; ks < DK / KW; ++ks)
+      for (int nt = 0; nt < NTB; ++nt) aD[nt] = aH[nt] = zero4();
 #pragma unroll
-        for (int nt = 0; nt < NTB; ++nt)
-          aD[nt] = Mma<T>::mma(wf[ks], frag_rowk(sHvk, LDK, 16 * nt, ks * KW), aD[nt]);
+      for (int ks = 0; ks < 64 / KW; ++ks)
 #pragma unroll
-      for (int nt = 0; nt < NTB; ++nt) store_acc_t2(sDeltaT, sDeltaTl, L64, rw, 16 * nt, aD[nt]);
+        for (int nt = 0; nt < NTB; ++nt) {
+          const frag bv = frag_colk_lds(sV, LDV, 16 * nt, ks * KW);
+          aD[nt] = Mma<T>::mma(tbh[ks], bv, aD[nt]);
+          if constexpr (SPLIT) aD[nt] = Mma<T>::mma(tbl[ks], bv, aD[nt]);
+        }
+#pragma unroll
+      for (int ks = 0; ks < DK / KW; ++ks) {
+        const frag aw = frag_colk_lds(sWT, L64, rw, ks * KW);
+#pragma unroll
+        for (int nt = 0; nt < NTB; ++nt) aH[nt] = Mma<T>::mma(aw, frag_rowk(sHvk, LDK, 16 * nt, ks * KW), aH[nt]);
+      }
+#pragma unroll
+      for (int nt = 0; nt < NTB; ++nt) store_acc_t2(sDeltaT, sDeltaTl, L64, rw, 16 * nt, aD[nt] - aH[nt]);
     }
     // dQg += dO h^T ; dW -= dDelta h^T ; dT_V += dDelta V^T
 #pragma unroll
@@ -775,7 +797,7 @@ template <typename T, int DK>
 static size_t grad_smem() {
   constexpr int P = pad_of<T>();
   constexpr int LDK = DK + P, L64 = 64 + P, DVB = GRAD_DVB, LDV = DVB + P;
-  constexpr int PH1 = (2 * DVB * LDK + 3 * DVB * L64 + 64 * LDV) * (int)sizeof(T);
+  constexpr int PH1 = (2 * DVB * LDK + 3 * DVB * L64 + 64 * LDV + DK * L64) * (int)sizeof(T);
   constexpr int PH2 = (2 * 64 * LDK + DK * L64 + 64 * L64) * (int)sizeof(T);
   return 64 * L64 * sizeof(T) + (4 * 64 + 2 * 4 * 64 + 8) * 4 + cmax(PH1, PH2);
 }

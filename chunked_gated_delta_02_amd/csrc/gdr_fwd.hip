@@ -158,7 +158,8 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
   RowBuf<T, DK> qbuf;
   RowBuf<T, DVB> vbuf;
   qbuf.load((const T*)a.q + rowq * DK, (int64_t)H * DK, len);
-  vbuf.load(vp + rowq * DV, (int64_t)H * DV, len);
+  // first V block for U, or (backward without U) the first dO block
+  vbuf.load(BWD && !a.Ua ? (const T*)a.dO + rowq * DV : vp + rowq * DV, (int64_t)H * DV, len);
   __syncthreads();
 
   // A = strictly_lower(diag(beta) K K^T * Gam): rows 16w, 4 column tiles
@@ -231,11 +232,11 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
     __syncthreads();
   }
   if constexpr (BWD) {
-    // T in the io dtype, row-major: the gradient kernel's operand copy
+    // T in fp32, row-major, for the gradient kernel
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = 4 * (tid + 256 * q);
-      store_acc4((T*)a.Tm + ch * 4096 + e, *reinterpret_cast<const f32x4*>(sTm + (e >> 6) * LDF + (e & 63)));
+      *reinterpret_cast<f32x4*>(a.Tm + ch * 4096 + e) = *reinterpret_cast<const f32x4*>(sTm + (e >> 6) * LDF + (e & 63));
     }
   }
 
@@ -273,7 +274,7 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
       for (int nt = 0; nt < 4; ++nt) store_acc_t(sW, LDK, w * (DK / 4) + 16 * mt, 16 * nt, acc[mt][nt]);
   }
   __syncthreads();
-  copy_afrag<T, 64, DK, false>((T*)a.Wf + ch * 64 * DK, sW, LDK);
+  if (a.Wf) copy_afrag<T, 64, DK, false>((T*)a.Wf + ch * 64 * DK, sW, LDK);
   if constexpr (BWD) {
     copy_afrag<T, DK, 64, true>((T*)a.WTf + ch * DK * 64, sW, LDK);
     copy_afrag<T, 64, DK, false>((T*)a.Kf + ch * 64 * DK, sK, LDK);
@@ -281,8 +282,9 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
   if (a.KtTf) copy_afrag<T, DK, 64, true>((T*)a.KtTf + ch * DK * 64, sK, LDK);
 
   // U = T diag(beta) V per DV block (rows 16w, fp32, accumulator order);
-  // T diag(beta) is a split operand read from the fp32 T
-  {
+  // T diag(beta) is a split operand read from the fp32 T.  The backward
+  // needs U only to recompute the snapshots.
+  if (!BWD || a.Ua) {
     auto d2 = [&](int s) { return sb[s]; };
     for (int dv0 = 0; dv0 < DV; dv0 += DVB) {
       __syncthreads();

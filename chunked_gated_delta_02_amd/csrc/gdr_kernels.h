@@ -43,13 +43,13 @@ struct WyArgs {
   const float* beta;
   const float* g;
   float* gam;   // [GSTRIDE]: gamma, e^gamma, e^{gamma_L - gamma}
-  void* Wf;     // afrag<64, DK>: W (rows r, k = dk)
-  float* Ua;    // acc<64, DV> fp32: U
+  void* Wf;     // afrag<64, DK>: W (rows r, k = dk); backward: nullable
+  float* Ua;    // acc<64, DV> fp32: U; backward: nullable
   void* KtTf;   // afrag<DK, 64>: K^T (exact; nullable)
   void* Qf;     // afrag<64, DK>: Q (exact)                          (forward)
   void* Pf;     // afrag<64, 64>: P = Q K^T * Gam (rows r), hi part  (forward)
   void* Pfl;    // the lo part (bf16 only)                           (forward)
-  void* Tm;     // [64][64] row-major (io dtype): T                 (backward)
+  float* Tm;    // [64][64] row-major fp32: T                        (backward)
   void* WTf;    // afrag<DK, 64>: W^T                                (backward)
   void* Kf;     // afrag<64, DK>: K (exact)                          (backward)
   float* dDl;   // acc<64, DV> fp32: scale P^T dO                    (backward)
@@ -123,9 +123,8 @@ struct GradArgs {
   const void* dO;
   const float* beta;
   const float* gam;
-  const void* Wf;
-  const float* Ua;
-  const void* Tm;
+  const void* WTf;      // afrag<DK, 64>: W^T
+  const float* Tm;      // [64][64] row-major fp32: T
   const void* hs;
   const void* dhs;
   const void* dD;
