@@ -5,7 +5,8 @@ MI355X, through libgdr's C ABI.
 One step = gdr_chunk_fwd (saving the per-chunk state snapshots) followed by
 gdr_chunk_bwd on one batch of the fixed-length bf16 workload B=2, T=4096,
 H=16, DK=DV=128 (seeded synthetic inputs, resident in HBM before the timed
-region).  Prints ONE JSON line.  Per-kernel durations come from HIP events
+region; between timed steps, outside the timed intervals, a 512 MiB write
+evicts the Infinity Cache).  Prints ONE JSON line.  Per-kernel durations come from HIP events
 that libgdr records around each launch on the call's stream (opt-in
 diagnostic timers).  The dominant kernel's roofline uses its algorithmic
 bytes (operator inputs read and outputs written once) and GEMM flops; the
@@ -42,6 +43,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--h-store", choices=("f32", "f16", "bf16"), default=None,
                     help="snapshot dtype (default: the workload's)")
+    ap.add_argument("--flush-mib", type=int, default=512,
+                    help="between timed steps, write this many MiB to evict the 256 MB Infinity Cache "
+                         "(outside the timed intervals; 0 = no flush)")
     ap.add_argument("--recompute", action="store_true",
                     help="the forward keeps no state snapshots and the backward recomputes them "
                          "(default: the forward saves them for the backward)")
@@ -348,23 +352,28 @@ def main():
         bwd()
     torch.cuda.synchronize()
 
-    # timed region: K steps; libgdr records per-kernel events for each call
+    # timed region: K steps, each bracketed by its own events; libgdr records
+    # per-kernel events for each call.  Between steps (outside the brackets)
+    # a write of flush_mib MiB evicts the Infinity Cache, so no step starts
+    # with its inputs cached from the previous one.
+    flush = torch.empty(args.flush_mib * (1 << 18), dtype=torch.float32, device=dev) if args.flush_mib else None
     evs = [[[hip.event() for _ in range(2 * nk)] for _ in range(2)] for _ in range(args.steps)]
-    e0, e1 = hip.event(), hip.event()
+    sev = [(hip.event(), hip.event()) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_host0 = time.perf_counter()
-    hip.record(e0, stream)
     for s in range(args.steps):
+        if flush is not None:
+            flush.fill_(float(s))
+        hip.record(sev[s][0], stream)
         _lib.gdr_set_kernel_timers(evs[s][0])
         fwd()
         _lib.gdr_set_kernel_timers(evs[s][1])
         bwd()
+        hip.record(sev[s][1], stream)
     _lib.gdr_set_kernel_timers(None)
-    hip.record(e1, stream)
     torch.cuda.synchronize()
     t_host1 = time.perf_counter()
-    total_ms = hip.elapsed_ms(e0, e1)
-    ms_step = total_ms / args.steps
+    ms_step = sum(hip.elapsed_ms(a, b) for a, b in sev) / args.steps
     if args.calibrate_copy_mib:
         # scale reference for --pmc byte counters: fp32 elementwise multiply by
         # one, reading and writing calibrate_copy_mib MiB once each
@@ -391,6 +400,10 @@ def main():
         for ph in row:
             for e in ph:
                 hip.destroy(e)
+    for a_, b_ in sev:
+        hip.destroy(a_)
+        hip.destroy(b_)
+    del flush
 
     tokens = B * T
     NT = B * T * H
@@ -456,6 +469,7 @@ def main():
         "fwd_ms": round(fwd_ms, 4),
         "bwd_ms": round(bwd_ms, 4),
         "host_wall_ms_per_step": round((t_host1 - t_host0) * 1e3 / args.steps, 4),
+        "cache_flush_mib": args.flush_mib,
         "kernels": kernels,
         "roofline": roof,
         "cpu_baseline": None,
