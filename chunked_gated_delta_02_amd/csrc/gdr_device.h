@@ -90,21 +90,6 @@ __device__ __forceinline__ typename Mma<T>::frag frag_rowk(const T* p, int ld, i
   }
 }
 
-// RowK from global memory with rows >= nrows reading as zero.
-template <typename T>
-__device__ __forceinline__ typename Mma<T>::frag frag_rowk_masked(const T* p, int64_t ld, int i0,
-                                                                 int k0, int nrows) {
-  const int l = lane_id();
-  const int i = i0 + (l & 15);
-  if (i >= nrows) return Mma<T>::zero();
-  const T* q = p + (int64_t)i * ld + k0 + Mma<T>::KPL * (l >> 4);
-  if constexpr (Mma<T>::KPL == 8) {
-    return *reinterpret_cast<const bf16x8*>(q);
-  } else {
-    return *q;
-  }
-}
-
 // Raw buffer resource over the bytes [p, p + bytes).  The hardware range
 // check of raw buffers (stride 0) makes loads past the end return zero and
 // drops stores past it, so a chunk's rows beyond its length need no branch:

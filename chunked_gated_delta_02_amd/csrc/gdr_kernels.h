@@ -179,57 +179,6 @@ __device__ __forceinline__ void load_rows(T* s, int ld, const T* g, int64_t gstr
   b.store(s, ld);
 }
 
-template <typename T>
-__device__ __forceinline__ void store8(T* dst, const float* v) {
-  if constexpr (sizeof(T) == 2) {
-    typedef T t8 __attribute__((ext_vector_type(8)));
-    t8 w;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) w[j] = from_f32<T>(v[j]);
-    *reinterpret_cast<t8*>(dst) = w;
-  } else {
-    *reinterpret_cast<f32x4*>(dst) = (f32x4){v[0], v[1], v[2], v[3]};
-    *reinterpret_cast<f32x4*>(dst + 4) = (f32x4){v[4], v[5], v[6], v[7]};
-  }
-}
-
-// Write rows [0, RB) of an afrag<*, K> matrix (dst already points at the
-// first fragment of row tile i0 / 16) with element (i, k) = f(i, k).  Each
-// thread writes 16-byte pieces; consecutive threads write consecutive pieces.
-// With dlo (16-bit T only) the values are split: hi into dst, lo into dlo.
-template <typename T, int RB, int K, typename F>
-__device__ __forceinline__ void write_afrag(T* dst, F&& f, T* dlo = nullptr) {
-  constexpr int KW = Mma<T>::KW, KPL = Mma<T>::KPL;
-  constexpr int PE = 16 / sizeof(T);                // elements per piece
-  constexpr int NPIECE = RB * K / PE;
-  for (int p = threadIdx.x; p < NPIECE; p += blockDim.x) {
-    float v[PE];
-#pragma unroll
-    for (int j = 0; j < PE; ++j) {
-      const int off = p * PE + j;
-      const int fr = off / (64 * KPL), rem = off - fr * (64 * KPL);
-      const int l = rem / KPL, jj = rem - l * KPL;
-      const int m = fr / (K / KW), s = fr - m * (K / KW);
-      v[j] = f(16 * m + (l & 15), KW * s + KPL * (l >> 4) + jj);
-    }
-    if constexpr (PE == 8) {
-      typedef T t8 __attribute__((ext_vector_type(8)));
-      t8 w, wl;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        T h, lo;
-        split2<T>(v[j], h, lo);
-        w[j] = h;
-        wl[j] = lo;
-      }
-      *reinterpret_cast<t8*>(dst + (int64_t)p * PE) = w;
-      if (dlo) *reinterpret_cast<t8*>(dlo + (int64_t)p * PE) = wl;
-    } else {
-      *reinterpret_cast<f32x4*>(dst + (int64_t)p * PE) = (f32x4){v[0], v[1], v[2], v[3]};
-    }
-  }
-}
-
 // Copy an R x K matrix from LDS into afrag<R, K> order, one MFMA fragment
 // (64 lanes x 16 bytes for bf16) per wave step: element (i, k) is
 // src[i * ld + k] (RowK) or src[k * ld + i] (ColK).  4 waves.
