@@ -184,6 +184,9 @@ class Hip:
         ms = ctypes.c_float()
         rc = self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b)
         if rc != 0:
+            # an event that was never recorded (kernel not launched): clear
+            # the runtime's sticky error so later HIP calls do not report it
+            self.lib.hipGetLastError()
             raise RuntimeError("hipEventElapsedTime failed: %d" % rc)
         return float(ms.value)
 

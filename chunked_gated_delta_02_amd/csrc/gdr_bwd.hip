@@ -65,7 +65,9 @@ __global__ __launch_bounds__(256) void k_scan_bwd(const ScanBwdArgs a) {
   constexpr int KS64 = 64 / KW;
   constexpr int MTH = DK / 64;
   constexpr int NT = DVT / 16;
-  constexpr int S = sizeof(T) == 2 ? SCAN_STAGES : 2;  // fp32 fragments are 8x larger
+  // fp32 fragments are 8x larger; 32-column tiles take a 2-stage ring so
+  // that two waves fit on each SIMD
+  constexpr int S = sizeof(T) == 2 ? (DVT == 32 ? 2 : SCAN_STAGES) : 2;
   typedef typename Mma<T>::frag frag;
   __shared__ __align__(16) T sDH[DVT * LDH];               // dh^T (dv, dk), hi
   __shared__ __align__(16) T sDHl[SPLIT ? DVT * LDH : 1];  // lo

@@ -435,8 +435,9 @@ __global__ __launch_bounds__(MODE >= 2 ? 512 : 256) void k_scan_fwd(const ScanFw
   constexpr int MTH = DK / 64;
   constexpr int NT = DVT / 16;
   constexpr int NB = OUT ? 2 : 1;   // h^T / Delta^T buffers
-  // fp32 fragments are 8x larger: shallower ring
-  constexpr int S = sizeof(T) == 2 ? (OUT ? 2 : SCAN_STAGES) : (OUT ? 1 : 2);
+  // fp32 fragments are 8x larger: shallower ring; 32-column snapshot tiles
+  // take 2 stages so that two waves fit on each SIMD
+  constexpr int S = sizeof(T) == 2 ? (OUT || (MODE == 1 && DVT == 32) ? 2 : SCAN_STAGES) : (OUT ? 1 : 2);
   // raw operand slots per ring stage, shared by both roles
   constexpr int NXR = KS + MTH * KS64;            // W, K^T
   constexpr int NXO = KS + (SPLIT ? 2 : 1) * KS64;  // Q, P (hi, lo)
