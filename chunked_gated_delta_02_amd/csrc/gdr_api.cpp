@@ -149,12 +149,10 @@ gdr::Geo make_geo(const gdr_problem* p, const Plan& pl, const int32_t* cu, char*
 // Column tile of the serial scans.  A wider tile reads each chunk operand
 // once for more columns, a narrower one gives more workgroups: take the
 // widest that still gives one workgroup per compute unit (256 in all), among
-// the tiles that fit in registers without spilling (32 at most; the output
-// scan 16 with DK = 128).  The fp32 path always uses 16 (its operand
-// fragments are 8x larger per k).
-int pick_dvt(long units, int cols, bool f32, int dk, bool out = false) {
+// the tiles that fit in registers (32 at most).  The fp32 path always uses
+// 16 (its operand fragments are 8x larger per k).
+int pick_dvt(long units, int cols, bool f32) {
   if (f32) return 16;
-  if (out && dk == 128) return 16;
   return units * (cols / 32) >= 256 ? 32 : 16;
 }
 
@@ -245,12 +243,12 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, con
   const long units = (long)pl.N * p->cp_segments * p->heads;
   if (p->cp_segments > 1) {
     sa.summ = (float*)(ws + pl.summ); sa.hstart = (const float*)(ws + pl.hst);
-    GDR_LAUNCH(GDR_KERNEL_CP_SCAN_FWD, s, gdr::launch_scan_fwd(sa, pl.f32, p->h_store_dtype, p->dk, pick_dvt(units, p->dk + p->dv, pl.f32, p->dk), 0, s));
+    GDR_LAUNCH(GDR_KERNEL_CP_SCAN_FWD, s, gdr::launch_scan_fwd(sa, pl.f32, p->h_store_dtype, p->dk, pick_dvt(units, p->dk + p->dv, pl.f32), 0, s));
     gdr::CpChainArgs ca{geo, p->dk, p->dv, p->layout, 0, h0, (const float*)(ws + pl.summ), (float*)(ws + pl.hst)};
     GDR_LAUNCH(GDR_KERNEL_CP_CHAIN_FWD, s, gdr::launch_cp_chain(ca, s));
   }
   // mode 2 writes the snapshots to h_saved; mode 3 keeps none
-  GDR_LAUNCH(GDR_KERNEL_SCAN_FWD, s, gdr::launch_scan_fwd(sa, pl.f32, p->h_store_dtype, p->dk, pick_dvt(units, p->dv, pl.f32, p->dk, true), h_saved ? 2 : 3, s));
+  GDR_LAUNCH(GDR_KERNEL_SCAN_FWD, s, gdr::launch_scan_fwd(sa, pl.f32, p->h_store_dtype, p->dk, pick_dvt(units, p->dv, pl.f32), h_saved ? 2 : 3, s));
   return GDR_OK;
 }
 
@@ -282,8 +280,8 @@ gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, con
   gdr::Geo geo = make_geo(p, pl, cu_seqlens, ws);
   const void* hs = h_saved ? h_saved : (const void*)(ws + pl.hs);
   const long units = (long)pl.N * p->cp_segments * p->heads;
-  const int dvt = pick_dvt(units, p->dv, pl.f32, p->dk);
-  const int dvt_cp = pick_dvt(units, p->dk + p->dv, pl.f32, p->dk);
+  const int dvt = pick_dvt(units, p->dv, pl.f32);
+  const int dvt_cp = pick_dvt(units, p->dk + p->dv, pl.f32);
 
   if (p->varlen)
     GDR_LAUNCH(GDR_KERNEL_PLAN, s, gdr::launch_plan(cu_seqlens, pl.N, p->seqlen, pl.NCb, (int*)(ws + pl.seq_chunk), (int*)(ws + pl.chunk_seq), s));

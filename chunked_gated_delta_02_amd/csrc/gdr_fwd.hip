@@ -812,7 +812,7 @@ static hipError_t launch_scan_fwd_t(ScanFwdArgs a, int dvt, hipStream_t st) {
   if (units == 0) return hipSuccess;
   const int nthr = MODE >= 2 ? 512 : 256;
   if (dvt == 16) hipLaunchKernelGGL((k_scan_fwd<T, HS, DK, 16, MODE>), dim3(grid), dim3(nthr), 0, st, a);
-  else if constexpr (sizeof(T) == 2 && !(MODE >= 2 && DK == 128)) {
+  else if constexpr (sizeof(T) == 2) {
     if (dvt == 32) hipLaunchKernelGGL((k_scan_fwd<T, HS, DK, 32, MODE>), dim3(grid), dim3(nthr), 0, st, a);
     else return hipErrorInvalidValue;
   } else {
