@@ -149,10 +149,12 @@ gdr::Geo make_geo(const gdr_problem* p, const Plan& pl, const int32_t* cu, char*
 // Column tile of the serial scans.  A wider tile reads each chunk operand
 // once for more columns, a narrower one gives more workgroups: take the
 // widest that still gives one workgroup per compute unit (256 in all), among
-// the tiles that fit in registers (32 at most).  The fp32 path always uses
-// 16 (its operand fragments are 8x larger per k).
-int pick_dvt(long units, int cols, bool f32) {
+// the widths measured faster (64 for the forward output scan, 32 for the
+// others: at 64 their rings no longer fit two waves per SIMD).  The fp32
+// path always uses 16 (its operand fragments are 8x larger per k).
+int pick_dvt(long units, int cols, bool f32, bool out = false) {
   if (f32) return 16;
+  if (out && cols % 64 == 0 && units * (cols / 64) >= 256) return 64;
   return units * (cols / 32) >= 256 ? 32 : 16;
 }
 
@@ -248,7 +250,7 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, con
     GDR_LAUNCH(GDR_KERNEL_CP_CHAIN_FWD, s, gdr::launch_cp_chain(ca, s));
   }
   // mode 2 writes the snapshots to h_saved; mode 3 keeps none
-  GDR_LAUNCH(GDR_KERNEL_SCAN_FWD, s, gdr::launch_scan_fwd(sa, pl.f32, p->h_store_dtype, p->dk, pick_dvt(units, p->dv, pl.f32), h_saved ? 2 : 3, s));
+  GDR_LAUNCH(GDR_KERNEL_SCAN_FWD, s, gdr::launch_scan_fwd(sa, pl.f32, p->h_store_dtype, p->dk, pick_dvt(units, p->dv, pl.f32, true), h_saved ? 2 : 3, s));
   return GDR_OK;
 }
 

@@ -436,8 +436,10 @@ __global__ __launch_bounds__(MODE >= 2 ? 512 : 256) void k_scan_fwd(const ScanFw
   constexpr int NT = DVT / 16;
   constexpr int NB = OUT ? 2 : 1;   // h^T / Delta^T buffers
   // fp32 fragments are 8x larger: shallower ring; 32-column snapshot tiles
-  // take 2 stages so that two waves fit on each SIMD
-  constexpr int S = sizeof(T) == 2 ? (OUT || (MODE == 1 && DVT == 32) ? 2 : SCAN_STAGES) : (OUT ? 1 : 2);
+  // take 2 stages and 64-column output tiles 1, so that two waves fit on
+  // each SIMD
+  constexpr int S = sizeof(T) == 2 ? (OUT && DVT == 64 ? 1 : (OUT || (MODE == 1 && DVT == 32) ? 2 : SCAN_STAGES))
+                                   : (OUT ? 1 : 2);
   // raw operand slots per ring stage, shared by both roles
   constexpr int NXR = KS + MTH * KS64;            // W, K^T
   constexpr int NXO = KS + (SPLIT ? 2 : 1) * KS64;  // Q, P (hi, lo)
@@ -814,6 +816,10 @@ static hipError_t launch_scan_fwd_t(ScanFwdArgs a, int dvt, hipStream_t st) {
   if (dvt == 16) hipLaunchKernelGGL((k_scan_fwd<T, HS, DK, 16, MODE>), dim3(grid), dim3(nthr), 0, st, a);
   else if constexpr (sizeof(T) == 2) {
     if (dvt == 32) hipLaunchKernelGGL((k_scan_fwd<T, HS, DK, 32, MODE>), dim3(grid), dim3(nthr), 0, st, a);
+    else if constexpr (MODE >= 2) {   // 64-column tiles: output scans only
+      if (dvt == 64) hipLaunchKernelGGL((k_scan_fwd<T, HS, DK, 64, MODE>), dim3(grid), dim3(nthr), 0, st, a);
+      else return hipErrorInvalidValue;
+    }
     else return hipErrorInvalidValue;
   } else {
     return hipErrorInvalidValue;

@@ -282,7 +282,7 @@ def test_context_parallel_autograd():
 FULL = {
     "cfg1": (C[1], [0, 11]),
     "cfg2": (C[2], [5]),
-    "cfg4": (C[4].replace(B=1), [3]),
+    "cfg4": (C[4].replace(B=2), [3]),   # B=2: enough units for 64-column output tiles
 }
 
 
