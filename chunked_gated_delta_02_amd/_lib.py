@@ -6,12 +6,15 @@ built -- there is no fallback of any kind.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import threading
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgdr.so")
+# race-test build: same kernels, barriers that can delay chosen waves
+DELAY_LIB_PATH = os.path.join(HERE, "libgdr_delay.so")
 
 GDR_OK, GDR_ERR_INVALID_ARG, GDR_ERR_UNSUPPORTED, GDR_ERR_WORKSPACE, GDR_ERR_HIP = range(5)
 GDR_F32, GDR_BF16, GDR_F16 = 0, 1, 2
@@ -49,22 +52,24 @@ class GDRError(RuntimeError):
         self.status = status
 
 
-_lock = threading.Lock()
-_lib = None
+_lock = threading.RLock()
+_lib = None        # the library the calls below use by default
+_libs = {}         # every library opened, by path
+_override = None   # the library selected by using(), if any
 
 
-def load(path: str = LIB_PATH):
-    """Load libgdr.so; raises if it is missing (build it first)."""
-    global _lib
+def _open(path: str):
     with _lock:
-        if _lib is not None:
-            return _lib
+        if path in _libs:
+            return _libs[path]
         if not os.path.exists(path):
             raise RuntimeError(
-                "libgdr.so is not built (%s). Build it with "
+                "%s is not built. Build it with "
                 "`python -c 'import __graft_entry__ as g; g.build()'` or "
                 "`python chunked_gated_delta_02_amd/build.py`." % path)
-        lib = ctypes.CDLL(path)
+        # RTLD_LOCAL: a second build of the library (the race-test one) keeps
+        # its own kernels and host code
+        lib = ctypes.CDLL(path, mode=os.RTLD_LOCAL)
         P = ctypes.POINTER(gdr_problem)
         vp, fp, ip = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
         lib.gdr_check.argtypes = [P]
@@ -88,16 +93,47 @@ def load(path: str = LIB_PATH):
         lib.gdr_last_error.restype = ctypes.c_char_p
         lib.gdr_version.argtypes = []
         lib.gdr_version.restype = ctypes.c_int
-        _lib = lib
+        if hasattr(lib, "gdr_debug_set_delay"):
+            lib.gdr_debug_set_delay.argtypes = [ctypes.c_int] * 4
+            lib.gdr_debug_set_delay.restype = ctypes.c_int
+        _libs[path] = lib
         return lib
 
 
+def load(path: str = LIB_PATH):
+    """Load libgdr.so (or, on the first call, the build at `path`); raises if
+    it is missing (build it first)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            _lib = _open(path)
+        return _lib
+
+
+def _h():
+    return _override if _override is not None else load()
+
+
+@contextlib.contextmanager
+def using(path: str):
+    """Route every call made inside the block to the build at `path` (the
+    race-test build DELAY_LIB_PATH in the tests)."""
+    global _override
+    lib = _open(path)
+    prev = _override
+    _override = lib
+    try:
+        yield lib
+    finally:
+        _override = prev
+
+
 def status_string(status: int) -> str:
-    return load().gdr_status_string(int(status)).decode()
+    return _h().gdr_status_string(int(status)).decode()
 
 
 def last_error() -> str:
-    return load().gdr_last_error().decode()
+    return _h().gdr_last_error().decode()
 
 
 def _raise_on(status: int) -> int:
@@ -107,29 +143,29 @@ def _raise_on(status: int) -> int:
 
 
 def gdr_check(p: gdr_problem) -> int:
-    return load().gdr_check(ctypes.byref(p))
+    return _h().gdr_check(ctypes.byref(p))
 
 
 def gdr_fwd_workspace_bytes(p: gdr_problem) -> int:
-    return load().gdr_fwd_workspace_bytes(ctypes.byref(p))
+    return _h().gdr_fwd_workspace_bytes(ctypes.byref(p))
 
 
 def gdr_bwd_workspace_bytes(p: gdr_problem, have_h_saved: bool) -> int:
-    return load().gdr_bwd_workspace_bytes(ctypes.byref(p), int(bool(have_h_saved)))
+    return _h().gdr_bwd_workspace_bytes(ctypes.byref(p), int(bool(have_h_saved)))
 
 
 def gdr_h_saved_bytes(p: gdr_problem) -> int:
-    return load().gdr_h_saved_bytes(ctypes.byref(p))
+    return _h().gdr_h_saved_bytes(ctypes.byref(p))
 
 
 def gdr_version() -> int:
-    return load().gdr_version()
+    return _h().gdr_version()
 
 
 def gdr_chunk_fwd(p, q, k, v, beta, g, cu_seqlens, h0, o, hT, h_saved, ws, ws_bytes, stream,
                   check=True) -> int:
     """Raw call; all tensor arguments are integer device addresses (0 = NULL)."""
-    st = load().gdr_chunk_fwd(ctypes.byref(p), q, k, v, beta, g, cu_seqlens or None, h0 or None, o,
+    st = _h().gdr_chunk_fwd(ctypes.byref(p), q, k, v, beta, g, cu_seqlens or None, h0 or None, o,
                               hT or None, h_saved or None, ws or None, ws_bytes, stream or None)
     return _raise_on(st) if check else st
 
@@ -137,7 +173,7 @@ def gdr_chunk_fwd(p, q, k, v, beta, g, cu_seqlens, h0, o, hT, h_saved, ws, ws_by
 def gdr_chunk_bwd(p, q, k, v, beta, g, cu_seqlens, h0, h_saved, dO, dhT, dq, dk, dv, dbeta, dg,
                   dh0, ws, ws_bytes, stream, check=True) -> int:
     """Raw call; all tensor arguments are integer device addresses (0 = NULL)."""
-    st = load().gdr_chunk_bwd(ctypes.byref(p), q, k, v, beta, g, cu_seqlens or None, h0 or None,
+    st = _h().gdr_chunk_bwd(ctypes.byref(p), q, k, v, beta, g, cu_seqlens or None, h0 or None,
                               h_saved or None, dO, dhT or None, dq, dk, dv, dbeta, dg, dh0 or None,
                               ws or None, ws_bytes, stream or None)
     return _raise_on(st) if check else st
@@ -147,7 +183,16 @@ def gdr_set_kernel_timers(events) -> int:
     """events: None, or a sequence of 2 * len(KERNELS) hipEvent_t handles
     (ints, 0 = not timed) -- (start, stop) per kernel id."""
     if events is None:
-        return _raise_on(load().gdr_set_kernel_timers(None))
+        return _raise_on(_h().gdr_set_kernel_timers(None))
     assert len(events) == 2 * len(KERNELS)
     arr = (ctypes.c_void_p * len(events))(*[e or None for e in events])
-    return _raise_on(load().gdr_set_kernel_timers(arr))
+    return _raise_on(_h().gdr_set_kernel_timers(arr))
+
+
+def gdr_debug_set_delay(wave: int, mod: int, iters: int, salt: int = 0) -> int:
+    """Barrier delays of the race-test build (include/libgdr_debug.h); only
+    that build exports it."""
+    lib = _h()
+    if not hasattr(lib, "gdr_debug_set_delay"):
+        raise RuntimeError("gdr_debug_set_delay: only the race-test build (libgdr_delay.so) exports it")
+    return _raise_on(lib.gdr_debug_set_delay(int(wave), int(mod), int(iters), int(salt)))

@@ -1,7 +1,9 @@
 """Build libgdr.so (HIP, gfx950) in-tree with hipcc.
 
 The library is compiled from ``csrc/*.hip`` and ``csrc/gdr_api.cpp`` into
-``chunked_gated_delta_02_amd/libgdr.so``.  After linking, the build checks
+``chunked_gated_delta_02_amd/libgdr.so``.  The same sources compiled with
+``-DGDR_DEBUG_DELAY`` give ``libgdr_delay.so``, the race-test build whose
+barriers can delay chosen waves (include/libgdr_debug.h); only tests load it.  After linking, the build checks
 that the shared object carries a gfx950 code object and that every kernel
 was compiled with non-trivial register usage (an empty kernel body is the
 signature of a build that silently dropped the target architecture).
@@ -20,6 +22,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libgdr.so")
+DELAY_LIB = os.path.join(HERE, "libgdr_delay.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -32,10 +35,10 @@ FLAGS = [
 ]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj,
-                             "-Rpass-analysis=kernel-resource-usage"]
+def _compile(src: str, verbose: bool, delay: bool = False) -> str:
+    obj = os.path.join(BUILD_DIR, os.path.basename(src) + (".delay.o" if delay else ".o"))
+    cmd = [HIPCC] + FLAGS + (["-DGDR_DEBUG_DELAY"] if delay else []) + [
+        "-c", os.path.join(CSRC, src), "-o", obj, "-Rpass-analysis=kernel-resource-usage"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s" % (src, r.stderr[-8000:]))
@@ -63,17 +66,25 @@ def _check_arch(lib: str) -> None:
         raise RuntimeError("%s carries no %s code object" % (lib, ARCH))
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s" % r.stderr[-8000:])
     _check_arch(tmp)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, delay: bool = True) -> str:
+    """Build libgdr.so and (delay=True) the race-test build libgdr_delay.so."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    jobs = [(s, False) for s in SOURCES] + ([(s, True) for s in SOURCES] if delay else [])
+    with cf.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        objs = list(ex.map(lambda j: _compile(j[0], verbose, j[1]), jobs))
+    _link(objs[:len(SOURCES)], LIB)
+    if delay:
+        _link(objs[len(SOURCES):], DELAY_LIB)
     return LIB
 
 

@@ -363,4 +363,18 @@ gdr_status gdr_set_kernel_timers(void* const* events) {
 
 int gdr_version(void) { return 100; }
 
+#ifdef GDR_DEBUG_DELAY
+gdr_status gdr_debug_set_delay(int wave, int mod, int iters, int salt) {
+  g_err[0] = 0;
+  if (wave < -1 || wave > 7 || mod < 1 || iters < 0 || iters > 64) {
+    set_err("delay settings out of range (wave %d, mod %d, iters %d)", wave, mod, iters);
+    return GDR_ERR_INVALID_ARG;
+  }
+  const gdr::DelayCfg c{wave, mod, iters, salt};
+  GDR_TRY(gdr::debug_set_delay_fwd(c));
+  GDR_TRY(gdr::debug_set_delay_bwd(c));
+  return GDR_OK;
+}
+#endif
+
 }  // extern "C"

@@ -152,7 +152,7 @@ __global__ __launch_bounds__(256) void k_scan_bwd(const ScanBwdArgs a) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) store_acc4(db + acc_off(dkw / 16 + mt, dv0 / 16 + nt, DV), acc_h[mt][nt]);
     }
-    __syncthreads();  // dh^T complete; last chunk's readers of dDelta^T are done
+    GDR_SYNC();  // dh^T complete; last chunk's readers of dDelta^T are done
     // dDelta = E (K dh) + scale P^T dO, rows 16w
     f32x4 acc_d[NT];
 #pragma unroll
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(256) void k_scan_bwd(const ScanBwdArgs a) {
       if constexpr (MODE != 0) store_acc4((T*)a.dD + ch * 64 * DV + acc_off(w, dv0 / 16 + nt, DV), acc_d[nt]);
       store_acc_t2(sDD, sDDl, LDD, rw, 16 * nt, -acc_d[nt]);
     }
-    __syncthreads();  // -dDelta^T complete; all readers of dh^T are done
+    GDR_SYNC();  // -dDelta^T complete; all readers of dh^T are done
     // dh <- e^{gamma_L} dh + scale Qg^T dO - W^T dDelta
 #pragma unroll
     for (int mt = 0; mt < MTH; ++mt)
@@ -345,7 +345,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
 
   // T diag(beta) (rows 16w) as a split operand of U = T diag(beta) V, read
   // from the fp32 T once the gates are in LDS
-  __syncthreads();
+  GDR_SYNC();
   frag tbh[64 / KW], tbl[64 / KW];
 #pragma unroll
   for (int ks = 0; ks < 64 / KW; ++ks) frag_rowk_f32<T>(Tg, 64, rw, ks * KW, [&](int s2) { return sb[s2]; }, tbh[ks], tbl[ks]);
@@ -358,7 +358,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
   const int64_t rowq = (int64_t)t0 * H + h;   // token-row index of chunk row 0
   for (int dvb = 0; dvb < DV; dvb += DVB) {
     frag dof[DVB / KW];     // dO fragments (rows 16w, k = dv)
-    __syncthreads();
+    GDR_SYNC();
     // h and dh (accumulator order <DK, DV>) and dDelta (accumulator order
     // <64, DV>) of this DV block, transposed into (dv, .) rows in LDS;
     // <dh, h> (for e^{gamma_L} <dh, h>) uses h in its stored precision
@@ -410,7 +410,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
       }
     }
     load_rows<T, DVB>(sV, LDV, vp + rowq * DV + dvb, (int64_t)H * DV, len);
-    __syncthreads();
+    GDR_SYNC();
     // Delta block = U - W h = T diag(beta) V - W h  (rows 16w)
     {
       f32x4 aD[NTB], aH[NTB];
@@ -447,7 +447,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) aTV[nt] = Mma<T>::mma(ddp, frag_rowk(sV, LDV, 16 * nt, ks * KW), aTV[nt]);
     }
-    __syncthreads();  // Delta^T complete
+    GDR_SYNC();  // Delta^T complete
     // dKt += Delta dh^T ; dP += dO Delta^T  (Delta split)
 #pragma unroll
     for (int ks = 0; ks < DVB / KW; ++ks) {
@@ -497,7 +497,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
   }
 
   // ---------------- phase 2 ----------------
-  __syncthreads();
+  GDR_SYNC();
   load_rows<T, DK>(sQ, LDK, qp + rowq * DK, (int64_t)H * DK, len);
   load_rows<T, DK>(sK, LDK, kp + rowq * DK, (int64_t)H * DK, len);
   // dW^T -> LDS (aW holds dW rows 16w)
@@ -523,7 +523,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
     }
     store_acc_t(sdQKT, L64, rw, 16 * nt, dq4);
   }
-  __syncthreads();
+  GDR_SYNC();
 
   // dgamma from P: rowsum - colsum of dP * P,  P = Q K^T * Gam
   {
@@ -639,11 +639,11 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
         aT[nt][i] = aTV[nt][i] * sb[s] + aT[nt][i] * sb[s] * seg[s];
       }
   }
-  __syncthreads();  // all reads of sQ, sdQKT, sdWT done
+  GDR_SYNC();  // all reads of sQ, sdQKT, sdWT done
   T* sTT = sQ;      // dT^T (s, r)
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) store_acc_t(sTT, L64, rw, 16 * nt, aT[nt]);
-  __syncthreads();
+  GDR_SYNC();
   // Y = T^T dT (rows a = 16w) -> LDS as Y^T
   {
     f32x4 aY[4];
@@ -659,7 +659,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) store_acc_t(sYT, L64, rw, 16 * nt, aY[nt]);
   }
-  __syncthreads();
+  GDR_SYNC();
   // dA = -(Y T^T) strictly lower; K K^T; dbeta, dgamma terms; G -> LDS as G^T
   {
     const T* sYT = sdQKT;
@@ -713,7 +713,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
       sMisc[4 + w] = xy;
     }
   }
-  __syncthreads();
+  GDR_SYNC();
   // dk += G K + G^T K, write dk
   {
     const T* sGT = sdWT;
@@ -739,7 +739,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
     rg[i] = sum16(rg[i]);
     rb[i] = sum16(rb[i]);
   }
-  __syncthreads();
+  GDR_SYNC();
   float* sRG = (float*)sQ;        // phase-2 LDS is free now
   float* sRB = sRG + 64;
   if ((l & 15) == 0) {
@@ -749,7 +749,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
       sRB[r0 + i] = rb[i];
     }
   }
-  __syncthreads();
+  GDR_SYNC();
   if (w == 0) {
     float dgam = sRG[l] - (sRed[0 * 256 + 0 * 64 + l] + sRed[0 * 256 + 1 * 64 + l] + sRed[0 * 256 + 2 * 64 + l] +
                            sRed[0 * 256 + 3 * 64 + l]) -
@@ -819,5 +819,12 @@ hipError_t launch_grad(const GradArgs& a, bool f32, int hs_dtype, int DK, hipStr
   if (hs_dtype == GDR_F16) return DK == 64 ? launch_grad_t<bf16, f16, 64>(a, st) : launch_grad_t<bf16, f16, 128>(a, st);
   return DK == 64 ? launch_grad_t<bf16, bf16, 64>(a, st) : launch_grad_t<bf16, bf16, 128>(a, st);
 }
+
+#ifdef GDR_DEBUG_DELAY
+// the race-test build: this file's copy of the barrier-delay settings
+hipError_t debug_set_delay_bwd(const DelayCfg& c) {
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_delay), &c, sizeof(c));
+}
+#endif
 
 }  // namespace gdr

@@ -484,4 +484,37 @@ __device__ __forceinline__ bool unit_of(int b, int units, int ntiles, int& p, in
   return p < units;
 }
 
+// ---------------------------------------------------------------------------
+// Workgroup barrier of every kernel.  The race-test build of the library
+// (compiled with GDR_DEBUG_DELAY) puts chosen waves to sleep after a
+// pseudo-random subset of barriers: a wave that reads or overwrites LDS
+// data another wave still needs, without a barrier in between, then sees
+// different data and the results change.  The sleeps change no arithmetic,
+// so that build's outputs with and without delays must be bitwise equal.
+#ifdef GDR_DEBUG_DELAY
+struct DelayCfg {
+  int wave;    // wave to delay, -1: every wave
+  int mod;     // delay after a barrier when a cycle-counter hash % mod == 0
+  int iters;   // s_sleep(127) repetitions per delay; 0 turns delays off
+  int salt;    // varies the pseudo-random choice between runs
+};
+// one copy per translation unit, written by the host before a launch
+static __constant__ DelayCfg g_delay;
+__device__ __forceinline__ void debug_delay() {
+  const DelayCfg c = g_delay;
+  if (c.iters <= 0 || c.mod <= 0) return;
+  if (c.wave >= 0 && c.wave != wave_id()) return;
+  const uint32_t t = (uint32_t)(__builtin_readcyclecounter() >> 6) ^ (blockIdx.x * 2654435761u) ^ (uint32_t)c.salt;
+  if (t % (uint32_t)c.mod != 0) return;
+  for (int i = 0; i < c.iters; ++i) __builtin_amdgcn_s_sleep(127);
+}
+#define GDR_SYNC()          \
+  do {                      \
+    __syncthreads();        \
+    ::gdr::debug_delay();   \
+  } while (0)
+#else
+#define GDR_SYNC() __syncthreads()
+#endif
+
 }  // namespace gdr

@@ -50,13 +50,13 @@ __global__ __launch_bounds__(1024) void k_plan(const int* cu, int N, int T_total
     }
   }
   s_part[tid] = local;
-  __syncthreads();
+  GDR_SYNC();
   // inclusive Hillis-Steele scan over 1024 partials
   for (int d = 1; d < 1024; d <<= 1) {
     const int v = (tid >= d) ? s_part[tid - d] : 0;
-    __syncthreads();
+    GDR_SYNC();
     s_part[tid] += v;
-    __syncthreads();
+    GDR_SYNC();
   }
   int run = s_part[tid] - local;
   for (int i = 0; i < per; ++i) {
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(1024) void k_plan(const int* cu, int N, int T_total
     }
   }
   if (tid == 1023) s_off[N] = min(s_part[1023], nchunks);
-  __syncthreads();
+  GDR_SYNC();
   for (int n = tid; n <= N; n += 1024) seq_chunk[n] = s_off[n];
   const int total = s_off[N];
   for (int c = tid; c < nchunks; c += 1024) {
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
   qbuf.load((const T*)a.q + rowq * DK, (int64_t)H * DK, len);
   // first V block for U, or (backward without U) the first dO block
   vbuf.load(BWD && !a.Ua ? (const T*)a.dO + rowq * DV : vp + rowq * DV, (int64_t)H * DV, len);
-  __syncthreads();
+  GDR_SYNC();
 
   // A = strictly_lower(diag(beta) K K^T * Gam): rows 16w, 4 column tiles
   {
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
         sA[r * LDF + s] = (s < r) ? sb[r] * acc[nt][i] * exp2_hw(sg[r] - sg[s]) : 0.f;
       }
   }
-  __syncthreads();
+  GDR_SYNC();
 
   // diagonal 16 x 16 blocks of T by forward substitution (wave 0: lane =
   // (block, column)); strictly-upper blocks are zero
@@ -202,7 +202,7 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
     const int r = e >> 6, s = e & 63;
     if ((s >> 4) > (r >> 4)) sTm[r * LDF + s] = 0.f;
   }
-  __syncthreads();
+  GDR_SYNC();
   // off-diagonal block rows (fp32 MFMA, k = 4 per instruction)
   for (int bi = 1; bi < 4; ++bi) {
     if (w < bi) {
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) sX[w * 320 + (acc_row0() + i) * 20 + acc_col()] = X[i];
     }
-    __syncthreads();
+    GDR_SYNC();
     if (w < bi) {
       f32x4 Y = zero4();
 #pragma unroll
@@ -229,7 +229,7 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) sTm[(16 * bi + acc_row0() + i) * LDF + 16 * w + acc_col()] = -Y[i];
     }
-    __syncthreads();
+    GDR_SYNC();
   }
   if constexpr (BWD) {
     // T in fp32, row-major, for the gradient kernel
@@ -273,7 +273,7 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) store_acc_t(sW, LDK, w * (DK / 4) + 16 * mt, 16 * nt, acc[mt][nt]);
   }
-  __syncthreads();
+  GDR_SYNC();
   if (a.Wf) copy_afrag<T, 64, DK, false>((T*)a.Wf + ch * 64 * DK, sW, LDK);
   if constexpr (BWD) {
     copy_afrag<T, DK, 64, true>((T*)a.WTf + ch * DK * 64, sW, LDK);
@@ -287,11 +287,11 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
   if (!BWD || a.Ua) {
     auto d2 = [&](int s) { return sb[s]; };
     for (int dv0 = 0; dv0 < DV; dv0 += DVB) {
-      __syncthreads();
+      GDR_SYNC();
       vbuf.store(sV, LDV);
       if (dv0 + DVB < DV) vbuf.load(vp + rowq * DV + dv0 + DVB, (int64_t)H * DV, len);
       else if constexpr (BWD) vbuf.load((const T*)a.dO + rowq * DV, (int64_t)H * DV, len);   // first dO block
-      __syncthreads();
+      GDR_SYNC();
       f32x4 acc[DVB / 16];
 #pragma unroll
       for (int nt = 0; nt < DVB / 16; ++nt) acc[nt] = zero4();
@@ -312,9 +312,9 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
     }
   }
 
-  __syncthreads();  // W staging, T and V are dead from here
+  GDR_SYNC();  // W staging, T and V are dead from here
   qbuf.store(sQ, LDK);
-  __syncthreads();
+  GDR_SYNC();
   // forward: P = Q K^T * Gam (rows r = 16w); backward: P^T (rows s = 16w);
   // diagonal included, staged fp32 in its own orientation
   {
@@ -340,7 +340,7 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
       store_acc(sPT, LDF, 16 * w, 16 * nt, acc[nt]);
     }
   }
-  __syncthreads();
+  GDR_SYNC();
   if constexpr (!BWD) {
     copy_afrag_split<T, 64, 64>((T*)a.Pf + ch * 4096, SPLIT ? (T*)a.Pfl + ch * 4096 : nullptr, sPT, LDF);
     copy_afrag<T, 64, DK, false>((T*)a.Qf + ch * 64 * DK, sQ, LDK);
@@ -354,10 +354,10 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
     auto qs = [&](int r) { return sc * seg[r]; };
     constexpr int MT = DK / 64;
     for (int dv0 = 0; dv0 < DV; dv0 += DVB) {
-      __syncthreads();
+      GDR_SYNC();
       vbuf.store(sV, LDV);
       if (dv0 + DVB < DV) vbuf.load(dop + rowq * DV + dv0 + DVB, (int64_t)H * DV, len);
-      __syncthreads();
+      GDR_SYNC();
       f32x4 accp[DVB / 16], accz[MT][DVB / 16];
 #pragma unroll
       for (int nt = 0; nt < DVB / 16; ++nt) {
@@ -547,7 +547,7 @@ __global__ __launch_bounds__(MODE >= 2 ? 512 : 256) void k_scan_fwd(const ScanFw
           for (int nt = 0; nt < NT; ++nt) store_acc4(hsb + acc_off(dkw / 16 + mt, dv0 / 16 + nt, DV), acc_h[mt][nt]);
       }
     }
-    __syncthreads();  // h^T of this chunk is complete
+    GDR_SYNC();  // h^T of this chunk is complete
     f32x4 acc_o[NT];
     if (!orole) {
       // Delta = U - W h (rows 16w)
@@ -582,7 +582,7 @@ __global__ __launch_bounds__(MODE >= 2 ? 512 : 256) void k_scan_fwd(const ScanFw
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc_o[nt] *= o.v[NT];
     }
-    __syncthreads();  // Delta^T complete; all readers of the other h^T buffer are done
+    GDR_SYNC();  // Delta^T complete; all readers of the other h^T buffer are done
     if (!orole) {
       // h <- e^{gamma_L} h + K^T (E Delta)
 #pragma unroll
@@ -747,7 +747,7 @@ __global__ __launch_bounds__(256) void k_cp_chain(const CpChainArgs a) {
     const float* Sb = summ(s);
 #pragma unroll
     for (int r = 0; r < RPT; ++r) acc[r] = Sb[(int64_t)(r0 + r) * W + DK + dv0 + j];
-    __syncthreads();  // S in this buffer and X are complete
+    GDR_SYNC();  // S in this buffer and X are complete
     for (int m = 0; m < DK; m += 4) {
       const float x0 = sX[m * 16 + j], x1 = sX[(m + 1) * 16 + j];
       const float x2 = sX[(m + 2) * 16 + j], x3 = sX[(m + 3) * 16 + j];
@@ -760,7 +760,7 @@ __global__ __launch_bounds__(256) void k_cp_chain(const CpChainArgs a) {
         acc[r] = fmaf(mv[3], x3, acc[r]);
       }
     }
-    __syncthreads();  // all reads of X and of this S buffer done
+    GDR_SYNC();  // all reads of X and of this S buffer done
     if (it + 1 < CP - 1) stash(sM + ((it + 1) & 1) * DK * LDM);
     float* ob = a.out + ((int64_t)so * N * H + n * H + h) * DK * DV;
 #pragma unroll
@@ -861,5 +861,12 @@ hipError_t launch_cp_chain(const CpChainArgs& a, hipStream_t st) {
   if (a.geo.N * a.geo.H == 0 || a.geo.cp <= 1) return hipSuccess;
   return a.DK == 64 ? launch_cp_chain_t<64>(a, st) : launch_cp_chain_t<128>(a, st);
 }
+
+#ifdef GDR_DEBUG_DELAY
+// the race-test build: this file's copy of the barrier-delay settings
+hipError_t debug_set_delay_fwd(const DelayCfg& c) {
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_delay), &c, sizeof(c));
+}
+#endif
 
 }  // namespace gdr

@@ -234,5 +234,10 @@ hipError_t launch_scan_fwd(const ScanFwdArgs& a, bool f32, int hs_dtype, int DK,
 hipError_t launch_scan_bwd(const ScanBwdArgs& a, bool f32, int DK, int dvt, int mode, hipStream_t st);
 hipError_t launch_cp_chain(const CpChainArgs& a, hipStream_t st);
 hipError_t launch_grad(const GradArgs& a, bool f32, int hs_dtype, int DK, hipStream_t st);
+#ifdef GDR_DEBUG_DELAY
+// barrier-delay settings of the kernels in each source file (race-test build)
+hipError_t debug_set_delay_fwd(const DelayCfg& c);
+hipError_t debug_set_delay_bwd(const DelayCfg& c);
+#endif
 
 }  // namespace gdr

@@ -27,6 +27,27 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(gdr_[a-z_0-9]+)\s*\(", text)))
 
 
+def test_race_build_exports_the_delay_hook_and_production_does_not(lib):
+    # libgdr_delay.so: every libgdr.h function plus gdr_debug_set_delay
+    # (include/libgdr_debug.h); libgdr.so: not the hook
+    assert not hasattr(lib, "gdr_debug_set_delay")
+    if not os.path.exists(_lib.DELAY_LIB_PATH):
+        from chunked_gated_delta_02_amd import build
+        build.build()
+    with _lib.using(_lib.DELAY_LIB_PATH) as d:
+        for n in _lib.EXPORTS + ("gdr_debug_set_delay",):
+            assert ctypes.cast(getattr(d, n), ctypes.c_void_p).value, n
+        text = open(os.path.join(ROOT, "include", "libgdr_debug.h")).read()
+        assert "gdr_debug_set_delay(" in text
+        # settings out of range are refused on the host, before any device call
+        for args in ((8, 1, 1), (-2, 1, 1), (0, 0, 1), (0, 1, -1), (0, 1, 65)):
+            with pytest.raises(_lib.GDRError) as e:
+                _lib.gdr_debug_set_delay(*args)
+            assert e.value.status == _lib.GDR_ERR_INVALID_ARG
+    with pytest.raises(RuntimeError):
+        _lib.gdr_debug_set_delay(0, 1, 0)
+
+
 def good(**kw):
     p = _lib.gdr_problem()
     p.batch, p.seqlen, p.num_seqs, p.varlen, p.heads = 2, 4096, 2, 0, 16
