@@ -97,8 +97,12 @@ __global__ __launch_bounds__(1024) void k_plan(const int* cu, int N, int T_total
 //   forward:  W, U (fp32), K^T, Q, P (hi + lo)
 //   backward: W, U, T, W^T, K, scale P^T dO and scale (e^gamma Q)^T dO (fp32)
 //             (+ K^T when the forward states are recomputed)
-// LDS: sK | RA = {A fp32, then W, then Q} | RT = {T fp32, then P^T fp32} |
-//      sV (V / dO block) | sX | gate vectors.
+// LDS (three tiles, so that three workgroups share a compute unit at DK = 128):
+//   R0 = K (r, dk); backward: then the dO blocks, once P^T is formed
+//   R1 = A (fp32), turned into T in place; then P (forward) or P^T (backward)
+//   R2 = the off-diagonal scratch of T; then W staging; then the V blocks of
+//        U; then Q
+// and the gate vectors.
 template <typename T, int DK, bool BWD>
 __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
   constexpr int P = pad_of<T>();
@@ -108,19 +112,23 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
   constexpr int LDV = DVB + P;
   constexpr int KW = Mma<T>::KW;
   constexpr bool SPLIT = sizeof(T) == 2;
-  constexpr int RA = cmax(64 * LDF * 4, 64 * LDK * (int)sizeof(T));
+  constexpr int R0 = 64 * LDK * (int)sizeof(T);
+  constexpr int R1 = 64 * LDF * 4;
+  constexpr int R2 = cmax(64 * LDK * (int)sizeof(T), cmax(64 * LDV * (int)sizeof(T), 4 * 16 * 20 * 4));
+  static_assert(64 * LDV <= 64 * LDK, "the dO blocks reuse the K tile");
   typedef typename Mma<T>::frag frag;
   extern __shared__ __align__(16) char smem[];
   T* sK = (T*)smem;
-  char* ra = smem + 64 * LDK * sizeof(T);
-  float* sA = (float*)ra;                 // A (fp32), until T is built
-  T* sW = (T*)ra;                         // W (r, dk) staging
-  T* sQ = (T*)ra;                         // Q (r, dk), after W is written
-  float* sTm = (float*)(ra + RA);         // T (fp32), until U is done
-  float* sPT = sTm;                       // then P (r, s) (forward) or P^T (s, r) (backward), fp32
-  T* sV = (T*)(ra + RA + 64 * LDF * 4);   // V / dO block (r, dv)
-  float* sX = (float*)(sV + 64 * LDV);
-  float* sg = sX + 4 * 16 * 20;
+  float* sA = (float*)(smem + R0);        // A (fp32), overwritten by T
+  float* sTm = sA;                        // T (fp32), until U is done
+  float* sPT = sA;                        // then P (r, s) (forward) or P^T (s, r) (backward), fp32
+  char* r2 = smem + R0 + R1;
+  float* sX = (float*)r2;                 // off-diagonal blocks of T in the making
+  T* sW = (T*)r2;                         // W (r, dk) staging
+  T* sVu = (T*)r2;                        // V block (r, dv) of U
+  T* sQ = (T*)r2;                         // Q (r, dk)
+  T* sVd = sK;                            // dO block (r, dv) (backward, after P^T)
+  float* sg = (float*)(r2 + R2);
   float* sb = sg + 64;
   float* seg = sb + 64;
   float* sE = seg + 64;
@@ -183,8 +191,10 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
   }
   GDR_SYNC();
 
-  // diagonal 16 x 16 blocks of T by forward substitution (wave 0: lane =
-  // (block, column)); strictly-upper blocks are zero
+  // T = (I + A)^-1 in place of A (A is zero on and above the diagonal, so
+  // the strictly-upper blocks of T already are).  Diagonal 16 x 16 blocks by
+  // forward substitution (wave 0: lane = (block, column); a wave's LDS
+  // accesses are ordered, so every read of a block precedes its overwrite)
   if (w == 0) {
     const int b = l >> 4, c = l & 15;
     float x[16];
@@ -198,12 +208,10 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) sTm[(16 * b + i) * LDF + 16 * b + c] = x[i];
   }
-  for (int e = tid; e < 64 * 64; e += 256) {
-    const int r = e >> 6, s = e & 63;
-    if ((s >> 4) > (r >> 4)) sTm[r * LDF + s] = 0.f;
-  }
   GDR_SYNC();
-  // off-diagonal block rows (fp32 MFMA, k = 4 per instruction)
+  // off-diagonal block rows (fp32 MFMA, k = 4 per instruction): block row bi
+  // reads A's blocks (bi, kb < bi), still intact, and T's rows above it;
+  // T_{bi,j} replaces A_{bi,j} after the barrier that ends all reads of row bi
   for (int bi = 1; bi < 4; ++bi) {
     if (w < bi) {
       f32x4 X = zero4();
@@ -288,7 +296,7 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
     auto d2 = [&](int s) { return sb[s]; };
     for (int dv0 = 0; dv0 < DV; dv0 += DVB) {
       GDR_SYNC();
-      vbuf.store(sV, LDV);
+      vbuf.store(sVu, LDV);
       if (dv0 + DVB < DV) vbuf.load(vp + rowq * DV + dv0 + DVB, (int64_t)H * DV, len);
       else if constexpr (BWD) vbuf.load((const T*)a.dO + rowq * DV, (int64_t)H * DV, len);   // first dO block
       GDR_SYNC();
@@ -301,7 +309,7 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
         frag_rowk_f32<T>(sTm, LDF, 16 * w, ks, d2, ah, al);
 #pragma unroll
         for (int nt = 0; nt < DVB / 16; ++nt) {
-          const frag bv = frag_colk_lds(sV, LDV, 16 * nt, ks);
+          const frag bv = frag_colk_lds(sVu, LDV, 16 * nt, ks);
           acc[nt] = Mma<T>::mma(ah, bv, acc[nt]);
           if constexpr (SPLIT) acc[nt] = Mma<T>::mma(al, bv, acc[nt]);
         }
@@ -355,7 +363,7 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
     constexpr int MT = DK / 64;
     for (int dv0 = 0; dv0 < DV; dv0 += DVB) {
       GDR_SYNC();
-      vbuf.store(sV, LDV);
+      vbuf.store(sVd, LDV);
       if (dv0 + DVB < DV) vbuf.load(dop + rowq * DV + dv0 + DVB, (int64_t)H * DV, len);
       GDR_SYNC();
       f32x4 accp[DVB / 16], accz[MT][DVB / 16];
@@ -373,7 +381,7 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
         for (int mt = 0; mt < MT; ++mt) frag_colk_scaled<T>(sQ, LDK, w * (DK / 4) + 16 * mt, ks, qs, qh[mt], ql[mt]);
 #pragma unroll
         for (int nt = 0; nt < DVB / 16; ++nt) {
-          const frag bo = frag_colk_lds(sV, LDV, 16 * nt, ks);
+          const frag bo = frag_colk_lds(sVd, LDV, 16 * nt, ks);
           accp[nt] = Mma<T>::mma(ph, bo, accp[nt]);
           if constexpr (SPLIT) accp[nt] = Mma<T>::mma(pl, bo, accp[nt]);
 #pragma unroll
@@ -778,8 +786,8 @@ template <typename T, int DK, bool BWD>
 static size_t wy_smem() {
   constexpr int P = pad_of<T>();
   constexpr int LDK = DK + P, LDF = 68, DVB = dvb_of<T>(), LDV = DVB + P;
-  constexpr int RA = cmax(64 * LDF * 4, 64 * LDK * (int)sizeof(T));
-  return 64 * LDK * sizeof(T) + RA + 64 * LDF * 4 + 64 * LDV * sizeof(T) + 4 * 16 * 20 * 4 + 4 * 64 * 4;
+  constexpr int R2 = cmax(64 * LDK * (int)sizeof(T), cmax(64 * LDV * (int)sizeof(T), 4 * 16 * 20 * 4));
+  return 64 * LDK * sizeof(T) + 64 * LDF * 4 + R2 + 4 * 64 * 4;
 }
 
 template <typename T, int DK, bool BWD>
