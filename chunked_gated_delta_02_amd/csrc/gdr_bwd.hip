@@ -41,7 +41,8 @@ namespace gdr {
 // where the two dh-independent terms come precomputed in fp32 and
 // -dDelta^T goes to LDS as a split operand.  The per-chunk operands (K,
 // W^T, the two fp32 terms, the gate factors) are loaded raw into a ring of
-// SCAN_STAGES register sets, SCAN_STAGES - 1 chunks ahead.  Writes the dh
+// SCAN_STAGES register sets, SCAN_STAGES - 1 chunks ahead; each chunk issues
+// the next loads in pieces between the MFMA steps of its dh update.  Writes the dh
 // snapshot and dDelta (io dtype; the gradient kernel rounds its MFMA
 // operands to it anyway), both in accumulator order, and dh0.
 //   MODE 1: the reverse scan proper.
@@ -118,32 +119,39 @@ __global__ __launch_bounds__(256) void k_scan_bwd(const ScanBwdArgs a) {
     f32x4 ee;               // e^{gamma_L - gamma} of the lane's 4 rows
     float eL;               // e^{gamma_L}
   };
-  auto load_ops = [&](int c, Ops& o) {
+  // the operands of chunk c in four pieces: K, W^T, the fp32 terms, gates
+  auto load_piece = [&](int c, Ops& o, int piece) {
     const int64_t ch = chb + c;
-    const T* Kb = (const T*)a.Kf + ch * 64 * DK;
+    if (piece == 0) {
+      const T* Kb = (const T*)a.Kf + ch * 64 * DK;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) o.kf[ks] = frag_af<T, DK>(Kb, w, ks);
-    const T* Wb = (const T*)a.WTf + ch * DK * 64;
-#pragma unroll
-    for (int mt = 0; mt < MTH; ++mt)
-#pragma unroll
-      for (int ks = 0; ks < KS64; ++ks) o.wf[mt][ks] = frag_af<T, 64>(Wb, dkw / 16 + mt, ks);
-    // the two fp32 terms are read by this tile only: streaming loads
-    const float* Db = a.dDl + ch * 64 * DV;
-    const float* Zb = a.Z + ch * DK * DV;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      o.dl[nt] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Db + acc_off(w, dv0 / 16 + nt, DV)));
+      for (int ks = 0; ks < KS; ++ks) o.kf[ks] = frag_af<T, DK>(Kb, w, ks);
+    } else if (piece == 1) {
+      const T* Wb = (const T*)a.WTf + ch * DK * 64;
 #pragma unroll
       for (int mt = 0; mt < MTH; ++mt)
-        o.z[mt][nt] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Zb + acc_off(dkw / 16 + mt, dv0 / 16 + nt, DV)));
+#pragma unroll
+        for (int ks = 0; ks < KS64; ++ks) o.wf[mt][ks] = frag_af<T, 64>(Wb, dkw / 16 + mt, ks);
+    } else if (piece == 2) {
+      // the two fp32 terms are read by this tile only: streaming loads
+      const float* Db = a.dDl + ch * 64 * DV;
+      const float* Zb = a.Z + ch * DK * DV;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        o.dl[nt] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Db + acc_off(w, dv0 / 16 + nt, DV)));
+#pragma unroll
+        for (int mt = 0; mt < MTH; ++mt)
+          o.z[mt][nt] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Zb + acc_off(dkw / 16 + mt, dv0 / 16 + nt, DV)));
+      }
+    } else {
+      const float* gb = a.gam + ch * GSTRIDE;
+      o.ee = *reinterpret_cast<const f32x4*>(gb + 128 + rw + acc_row0());
+      o.eL = gb[64 + 63];
     }
-    const float* gb = a.gam + ch * GSTRIDE;
-    o.ee = *reinterpret_cast<const f32x4*>(gb + 128 + rw + acc_row0());
-    o.eL = gb[64 + 63];
   };
 
-  auto process = [&](int c, Ops& o) {
+  // chunk c from stage o; with pf, the operands of chunk cn go to stage on
+  auto process = [&](int c, Ops& o, int cn, Ops& on, bool pf) {
     const int64_t ch = chb + c;
     if constexpr (MODE != 0) {
       T* db = (T*)a.dhs + ch * DK * DV;
@@ -177,7 +185,16 @@ __global__ __launch_bounds__(256) void k_scan_bwd(const ScanBwdArgs a) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc_h[mt][nt] = acc_h[mt][nt] * o.eL + (mtile ? zero4() : o.z[mt][nt]);
 #pragma unroll
-    for (int ks = 0; ks < KS64; ++ks)
+    for (int ks = 0; ks < KS64; ++ks) {
+      // the prefetch is issued in pieces between these MFMA steps, where its
+      // issue overlaps the MFMA chain instead of delaying the next barrier
+      if (pf) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int pc = 0; pc < 4; ++pc)
+          if (pc * KS64 / 4 == ks) load_piece(cn, on, pc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const frag bd = frag_rowk(sDD, LDD, 16 * nt, ks * KW);
@@ -189,6 +206,7 @@ __global__ __launch_bounds__(256) void k_scan_bwd(const ScanBwdArgs a) {
           for (int mt = 0; mt < MTH; ++mt) acc_h[mt][nt] = Mma<T>::mma(o.wf[mt][ks], bdl, acc_h[mt][nt]);
         }
       }
+    }
 #pragma unroll
     for (int mt = 0; mt < MTH; ++mt)
 #pragma unroll
@@ -203,18 +221,18 @@ __global__ __launch_bounds__(256) void k_scan_bwd(const ScanBwdArgs a) {
   if (nc > 0) {
     Ops st[S];
 #pragma unroll
-    for (int s = 0; s < S - 1; ++s) load_ops(nc - 1 - min(s, nc - 1), st[s]);
+    for (int s = 0; s < S - 1; ++s)
+#pragma unroll
+      for (int pc = 0; pc < 4; ++pc) load_piece(nc - 1 - min(s, nc - 1), st[s], pc);
     int jb = 0;
     for (; jb + S <= nc; jb += S) {
 #pragma unroll
-      for (int s = 0; s < S; ++s) {
-        load_ops(nc - 1 - min(jb + s + S - 1, nc - 1), st[(s + S - 1) % S]);
-        process(nc - 1 - (jb + s), st[s]);
-      }
+      for (int s = 0; s < S; ++s)
+        process(nc - 1 - (jb + s), st[s], nc - 1 - min(jb + s + S - 1, nc - 1), st[(s + S - 1) % S], true);
     }
 #pragma unroll
     for (int s = 0; s < S - 1; ++s)
-      if (jb + s < nc) process(nc - 1 - (jb + s), st[s]);
+      if (jb + s < nc) process(nc - 1 - (jb + s), st[s], 0, st[s], false);
   }
   if (MODE == 0) {
 #pragma unroll
