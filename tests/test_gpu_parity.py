@@ -276,6 +276,36 @@ def test_context_parallel_autograd():
 
 
 # ---------------------------------------------------------------------------
+# the limits the boundary accepts: DV = 512 (widest value dimension), and
+# packed batches past one sequence per thread of the chunk-table kernel (its
+# scan handles ceil(N / 1024) sequences per thread) up to num_seqs = 8192
+
+LIMITS = {
+    "bf16_dv512": C[1].replace(name="bf16_dv512", B=1, T=200, H=2, DV=512, has_h0=True),
+    "fp32_dk64_dv512": C[0].replace(name="fp32_dk64_dv512", B=1, T=130, H=1, DK=64, DV=512, layout="KV"),
+}
+
+
+@pytest.mark.parametrize("case", sorted(LIMITS))
+def test_parity_widest_value_dimension(case):
+    w = LIMITS[case]
+    say("[case] %s" % case)
+    inp = gin.generate(w)
+    compare(w, run_gpu(w, inp), run_oracle(w, inp))
+
+
+@pytest.mark.parametrize("nseq,maxlen", [(3000, 20), (8192, 6)])
+def test_varlen_many_sequences(nseq, maxlen):
+    rng = np.random.default_rng(nseq)
+    lengths = [int(x) for x in rng.integers(0, maxlen + 1, size=nseq)]
+    lengths[-1] = 70   # a last sequence longer than one chunk
+    w = C[2].replace(name="varlen_n%d" % nseq, H=1, DK=64, DV=64, lengths=lengths, len_range=None)
+    say("[case] varlen %d sequences, %d tokens" % (nseq, sum(lengths)))
+    inp = gin.generate(w)
+    compare(w, run_gpu(w, inp), run_oracle(w, inp))
+
+
+# ---------------------------------------------------------------------------
 # full sizes of the workloads, the launch configuration the benchmark times,
 # checked on sampled heads (each head is an independent problem)
 
