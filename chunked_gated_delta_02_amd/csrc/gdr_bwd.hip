@@ -264,15 +264,21 @@ __global__ __launch_bounds__(256) void k_scan_bwd(const ScanBwdArgs a) {
 // stream mixes operand loads with the MFMA chain stalls at the loads
 // whenever the memory pipeline is backed up, and the whole chain waits at
 // the next barrier; here waves 0..3 run the recurrence exactly as k_scan_bwd
-// does but read their operands from LDS, and wave 4 only issues
-// global -> LDS loads (16 bytes per lane, one 1 KB fragment per instruction,
-// the fragment and accumulator orders of the workspace carried over
-// unchanged) into a ring of R chunk slots, D = R - 1 chunks ahead.  Before the
-// first barrier of step j the producer waits for chunk j's loads (vmcnt),
-// so after that barrier its slot is complete; it refills slot (j + D) % R,
-// last read at step j - 1, only after that barrier.
+// does but read their operands from LDS, and waves 4.. only issue global ->
+// LDS loads (16 bytes per lane, one 1 KB fragment per instruction, the
+// fragment and accumulator orders of the workspace carried over unchanged)
+// into a ring of R chunk slots, D = R - 1 chunks ahead.  A chunk's loads are
+// dealt round-robin to the SCAN_PRODUCERS producer waves, so that each keeps
+// two chunks in flight within its 63 outstanding vector-memory operations.
+// After the first barrier of step j a producer refills slot (j + D) % R,
+// whose operands the compute waves read during step j - 2; before the second
+// barrier it waits (vmcnt) for its loads of chunk j + 1, so after that
+// barrier the compute waves read chunk j + 1's operands while they update.
+#define SCAN_PRODUCERS 2
+template <int V> struct IntC { static constexpr int value = V; };
+
 template <int DK, int MODE>
-__global__ __launch_bounds__(320) void k_scan_bwd_p(const ScanBwdArgs a) {
+__global__ __launch_bounds__(64 * (4 + SCAN_PRODUCERS)) void k_scan_bwd_p(const ScanBwdArgs a) {
   typedef bf16 T;
   constexpr int DVT = 16;
   constexpr int P = pad_of<T>();
@@ -288,8 +294,9 @@ __global__ __launch_bounds__(320) void k_scan_bwd_p(const ScanBwdArgs a) {
   constexpr int NKF = 64 * DK / 512;   // 1 KB fragments of K (and of W^T)
   constexpr int OW = NKF * 1024, OD = 2 * NKF * 1024, OZ = OD + 4 * 1024, OG = OZ + (DK / 16) * 1024;
   constexpr int SLOT = OG + 512;
-  constexpr int L = 2 * NKF + 4 + DK / 16 + 1;   // producer loads per chunk
-  static_assert(L < 64, "vmcnt range");
+  constexpr int L = 2 * NKF + 4 + DK / 16 + 1;   // loads per chunk, all producers
+  constexpr int NP = SCAN_PRODUCERS;
+  static_assert(2 * ((L + NP - 1) / NP) < 64, "two chunks per producer within the vmcnt range");
   typedef typename Mma<T>::frag frag;
   __shared__ __align__(16) T sDH[DVT * LDH];    // dh^T (dv, dk), hi
   __shared__ __align__(16) T sDHl[DVT * LDH];   // lo
@@ -308,54 +315,70 @@ __global__ __launch_bounds__(320) void k_scan_bwd_p(const ScanBwdArgs a) {
   int c0, nc, ts, tl;
   seg_range(a.geo, n, sg, c0, nc, ts, tl);
   const int w = wave_id(), l = lane_id();
-  const bool producer = w == 4;
+  const bool producer = w >= 4;
   const int dkw = (w & 3) * (DK / 4);
   const int rw = 16 * (w & 3);
   const int64_t chb = (int64_t)h * a.geo.nchunks + c0;
 
-  // producer: chunk c's operands into slot sl
-  auto produce = [&](int c, int sl) {
+  // producer: load q (0 <= q < L) of chunk c's operands into slot sl
+  auto piece = [&](int c, int sl, int q) {
     typedef __attribute__((address_space(1))) const void* gptr;
     typedef __attribute__((address_space(3))) void* lptr;
     const int64_t ch = chb + c;
     char* sp = ring + sl * SLOT;
-    const T* Kb = (const T*)a.Kf + ch * 64 * DK;
-    const T* Wb = (const T*)a.WTf + ch * DK * 64;
-#pragma unroll
-    for (int f = 0; f < NKF; ++f)
-      __builtin_amdgcn_global_load_lds((gptr)(Kb + ((int64_t)f * 64 + l) * 8), (lptr)(sp + f * 1024), 16, 0, 0);
-#pragma unroll
-    for (int f = 0; f < NKF; ++f)
+    if (q < NKF) {
+      const T* Kb = (const T*)a.Kf + ch * 64 * DK;
+      __builtin_amdgcn_global_load_lds((gptr)(Kb + ((int64_t)q * 64 + l) * 8), (lptr)(sp + q * 1024), 16, 0, 0);
+    } else if (q < 2 * NKF) {
+      const T* Wb = (const T*)a.WTf + ch * DK * 64;
+      const int f = q - NKF;
       __builtin_amdgcn_global_load_lds((gptr)(Wb + ((int64_t)f * 64 + l) * 8), (lptr)(sp + OW + f * 1024), 16, 0, 0);
-    const float* Db = a.dDl + ch * 64 * DV;
-    const float* Zb = a.Z + ch * DK * DV;
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
+    } else if (q < 2 * NKF + 4) {
+      const float* Db = a.dDl + ch * 64 * DV;
+      const int m = q - 2 * NKF;
       __builtin_amdgcn_global_load_lds((gptr)(Db + acc_off(m, dv0 / 16, DV)), (lptr)(sp + OD + m * 1024), 16, 0, 0);
-#pragma unroll
-    for (int m = 0; m < DK / 16; ++m)
+    } else if (q < L - 1) {
+      const float* Zb = a.Z + ch * DK * DV;
+      const int m = q - 2 * NKF - 4;
       __builtin_amdgcn_global_load_lds((gptr)(Zb + acc_off(m, dv0 / 16, DV)), (lptr)(sp + OZ + m * 1024), 16, 0, 0);
-    // e^gamma and E: floats [64, 192) of the chunk's gate block, 32 lanes
-    if (l < 32)
+    } else if (l < 32) {
+      // e^gamma and E: floats [64, 192) of the chunk's gate block, 32 lanes
       __builtin_amdgcn_global_load_lds((gptr)(a.gam + ch * GSTRIDE + 64 + 4 * l), (lptr)(sp + OG), 16, 0, 0);
+    }
   };
-
-  if (producer) {
-    if (nc == 0) return;
+  auto run_producer = [&](auto pc) {
+    constexpr int pw = decltype(pc)::value;
+    constexpr int Lp = (L - pw + NP - 1) / NP;   // this wave's loads per chunk
+    auto produce = [&](int c, int sl) {
+#pragma unroll
+      for (int q = pw; q < L; q += NP) piece(c, sl, q);
+    };
 #pragma unroll
     for (int s = 0; s < D; ++s)
       if (s < nc) produce(nc - 1 - s, s);
     // chunk 0 has landed once at most the loads of chunk 1 are pending
-    if (1 < nc) wait_vmcnt<L>();
+    if (1 < nc) wait_vmcnt<Lp>();
     else wait_vmcnt<0>();
     GDR_BARRIER_ONLY();   // slot 0 complete
     for (int j = 0; j < nc; ++j) {
       GDR_BARRIER_ONLY();   // first barrier of step j: slot (j + D) % R is free
       if (j + D < nc) produce(nc - 1 - (j + D), (j + D) % R);
       // chunk j + 1 has landed once at most the loads of chunk j + 2 are pending
-      if (j + D < nc) wait_vmcnt<L>();
+      if (j + D < nc) wait_vmcnt<Lp>();
       else wait_vmcnt<0>();
       GDR_BARRIER_ONLY();   // second barrier of step j: slot (j + 1) % R is complete
+    }
+  };
+
+  if (producer) {
+    if (nc == 0) return;
+    if (w == 4) run_producer(IntC<0>());
+    else if constexpr (NP > 1) {
+      if (w == 5) run_producer(IntC<1>());
+      else if constexpr (NP > 2) {
+        if (w == 6) run_producer(IntC<2>());
+        else if constexpr (NP > 3) run_producer(IntC<3>());
+      }
     }
     return;
   }
@@ -1025,7 +1048,7 @@ static hipError_t launch_scan_bwd_p(ScanBwdArgs a, hipStream_t st) {
   const size_t sm = (size_t)3 * (2 * nkf * 1024 + 4 * 1024 + (DK / 16) * 1024 + 512);
   hipError_t e = hipFuncSetAttribute((const void*)k_scan_bwd_p<DK, MODE>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_scan_bwd_p<DK, MODE>), dim3(grid), dim3(320), sm, st, a);
+  hipLaunchKernelGGL((k_scan_bwd_p<DK, MODE>), dim3(grid), dim3(64 * (4 + SCAN_PRODUCERS)), sm, st, a);
   return hipGetLastError();
 }
 
