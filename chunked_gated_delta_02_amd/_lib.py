@@ -117,7 +117,8 @@ def _h():
 @contextlib.contextmanager
 def using(path: str):
     """Route every call made inside the block to the build at `path` (the
-    race-test build DELAY_LIB_PATH in the tests)."""
+    race-test build DELAY_LIB_PATH in the tests).  The switch is process-wide:
+    calls from other threads during the block go to that build too."""
     global _override
     lib = _open(path)
     prev = _override
