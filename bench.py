@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--flush-mib", type=int, default=512,
                     help="between timed steps, write this many MiB to evict the 256 MB Infinity Cache "
                          "(outside the timed intervals; 0 = no flush)")
+    ap.add_argument("--cp-segments", type=int, default=None,
+                    help="intra-card context-parallel segments per sequence (default: the workload's)")
     ap.add_argument("--recompute", action="store_true",
                     help="the forward keeps no state snapshots and the backward recomputes them "
                          "(default: the forward saves them for the backward)")
@@ -312,6 +314,8 @@ def main():
     w = gin.CONFIGS[args.config]
     if args.h_store:
         w = w.replace(h_store=args.h_store)
+    if args.cp_segments:
+        w = w.replace(cp_segments=args.cp_segments)
     inp = gin.generate(w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
