@@ -258,241 +258,6 @@ __global__ __launch_bounds__(256) void k_scan_bwd(const ScanBwdArgs a) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// k_scan_bwd_p: k_scan_bwd for bf16 operands at 16-column tiles, with the
-// per-chunk operands staged by a producer wave.  A wave whose instruction
-// stream mixes operand loads with the MFMA chain stalls at the loads
-// whenever the memory pipeline is backed up, and the whole chain waits at
-// the next barrier; here waves 0..3 run the recurrence exactly as k_scan_bwd
-// does but read their operands from LDS, and waves 4.. only issue global ->
-// LDS loads (16 bytes per lane, one 1 KB fragment per instruction, the
-// fragment and accumulator orders of the workspace carried over unchanged)
-// into a ring of R chunk slots, D = R - 1 chunks ahead.  A chunk's loads are
-// dealt round-robin to the SCAN_PRODUCERS producer waves, so that each keeps
-// two chunks in flight within its 63 outstanding vector-memory operations.
-// After the first barrier of step j a producer refills slot (j + D) % R,
-// whose operands the compute waves read during step j - 2; before the second
-// barrier it waits (vmcnt) for its loads of chunk j + 1, so after that
-// barrier the compute waves read chunk j + 1's operands while they update.
-#define SCAN_PRODUCERS 2
-template <int V> struct IntC { static constexpr int value = V; };
-
-template <int DK, int MODE>
-__global__ __launch_bounds__(64 * (4 + SCAN_PRODUCERS)) void k_scan_bwd_p(const ScanBwdArgs a) {
-  typedef bf16 T;
-  constexpr int DVT = 16;
-  constexpr int P = pad_of<T>();
-  constexpr int LDH = DK + P;
-  constexpr int LDD = 64 + P;
-  constexpr int KW = Mma<T>::KW;
-  constexpr int KS = DK / KW;
-  constexpr int KS64 = 64 / KW;
-  constexpr int MTH = DK / 64;
-  constexpr int R = 3, D = R - 1;
-  // slot layout (bytes): K fragments, W^T fragments, scale P^T dO tile
-  // (4 x 1 KB), scale Qg^T dO tile (DK / 16 x 1 KB), gates (e^gamma, E)
-  constexpr int NKF = 64 * DK / 512;   // 1 KB fragments of K (and of W^T)
-  constexpr int OW = NKF * 1024, OD = 2 * NKF * 1024, OZ = OD + 4 * 1024, OG = OZ + (DK / 16) * 1024;
-  constexpr int SLOT = OG + 512;
-  constexpr int L = 2 * NKF + 4 + DK / 16 + 1;   // loads per chunk, all producers
-  constexpr int NP = SCAN_PRODUCERS;
-  static_assert(2 * ((L + NP - 1) / NP) < 64, "two chunks per producer within the vmcnt range");
-  typedef typename Mma<T>::frag frag;
-  __shared__ __align__(16) T sDH[DVT * LDH];    // dh^T (dv, dk), hi
-  __shared__ __align__(16) T sDHl[DVT * LDH];   // lo
-  __shared__ __align__(16) T sDD[DVT * LDD];    // -dDelta^T (dv, r), hi
-  __shared__ __align__(16) T sDDl[DVT * LDD];   // lo
-  extern __shared__ __align__(16) char ring[];  // R slots of SLOT bytes
-
-  const int H = a.geo.H, DV = a.DV, CP = a.geo.cp, N = a.geo.N;
-  int p, jt;
-  if (!unit_of(blockIdx.x, N * CP * H, a.ntiles, p, jt)) return;
-  const int h = p % H, sg = (p / H) % CP, n = p / (H * CP);
-  if (MODE == 0 && sg == 0) return;        // the first segment hands nothing back
-  const int col0 = jt * DVT;
-  const bool mtile = MODE == 0 && col0 < DK;   // transition columns: start at I, no dO
-  const int dv0 = MODE == 0 ? (mtile ? 0 : col0 - DK) : col0;   // column of the dO terms
-  int c0, nc, ts, tl;
-  seg_range(a.geo, n, sg, c0, nc, ts, tl);
-  const int w = wave_id(), l = lane_id();
-  const bool producer = w >= 4;
-  const int dkw = (w & 3) * (DK / 4);
-  const int rw = 16 * (w & 3);
-  const int64_t chb = (int64_t)h * a.geo.nchunks + c0;
-
-  // producer: load q (0 <= q < L) of chunk c's operands into slot sl
-  auto piece = [&](int c, int sl, int q) {
-    typedef __attribute__((address_space(1))) const void* gptr;
-    typedef __attribute__((address_space(3))) void* lptr;
-    const int64_t ch = chb + c;
-    char* sp = ring + sl * SLOT;
-    if (q < NKF) {
-      const T* Kb = (const T*)a.Kf + ch * 64 * DK;
-      __builtin_amdgcn_global_load_lds((gptr)(Kb + ((int64_t)q * 64 + l) * 8), (lptr)(sp + q * 1024), 16, 0, 0);
-    } else if (q < 2 * NKF) {
-      const T* Wb = (const T*)a.WTf + ch * DK * 64;
-      const int f = q - NKF;
-      __builtin_amdgcn_global_load_lds((gptr)(Wb + ((int64_t)f * 64 + l) * 8), (lptr)(sp + OW + f * 1024), 16, 0, 0);
-    } else if (q < 2 * NKF + 4) {
-      const float* Db = a.dDl + ch * 64 * DV;
-      const int m = q - 2 * NKF;
-      __builtin_amdgcn_global_load_lds((gptr)(Db + acc_off(m, dv0 / 16, DV)), (lptr)(sp + OD + m * 1024), 16, 0, 0);
-    } else if (q < L - 1) {
-      const float* Zb = a.Z + ch * DK * DV;
-      const int m = q - 2 * NKF - 4;
-      __builtin_amdgcn_global_load_lds((gptr)(Zb + acc_off(m, dv0 / 16, DV)), (lptr)(sp + OZ + m * 1024), 16, 0, 0);
-    } else if (l < 32) {
-      // e^gamma and E: floats [64, 192) of the chunk's gate block, 32 lanes
-      __builtin_amdgcn_global_load_lds((gptr)(a.gam + ch * GSTRIDE + 64 + 4 * l), (lptr)(sp + OG), 16, 0, 0);
-    }
-  };
-  auto run_producer = [&](auto pc) {
-    constexpr int pw = decltype(pc)::value;
-    constexpr int Lp = (L - pw + NP - 1) / NP;   // this wave's loads per chunk
-    auto produce = [&](int c, int sl) {
-#pragma unroll
-      for (int q = pw; q < L; q += NP) piece(c, sl, q);
-    };
-#pragma unroll
-    for (int s = 0; s < D; ++s)
-      if (s < nc) produce(nc - 1 - s, s);
-    // chunk 0 has landed once at most the loads of chunk 1 are pending
-    if (1 < nc) wait_vmcnt<Lp>();
-    else wait_vmcnt<0>();
-    GDR_BARRIER_ONLY();   // slot 0 complete
-    for (int j = 0; j < nc; ++j) {
-      GDR_BARRIER_ONLY();   // first barrier of step j: slot (j + D) % R is free
-      if (j + D < nc) produce(nc - 1 - (j + D), (j + D) % R);
-      // chunk j + 1 has landed once at most the loads of chunk j + 2 are pending
-      if (j + D < nc) wait_vmcnt<Lp>();
-      else wait_vmcnt<0>();
-      GDR_BARRIER_ONLY();   // second barrier of step j: slot (j + 1) % R is complete
-    }
-  };
-
-  if (producer) {
-    if (nc == 0) return;
-    if (w == 4) run_producer(IntC<0>());
-    else if constexpr (NP > 1) {
-      if (w == 5) run_producer(IntC<1>());
-      else if constexpr (NP > 2) {
-        if (w == 6) run_producer(IntC<2>());
-        else if constexpr (NP > 3) run_producer(IntC<3>());
-      }
-    }
-    return;
-  }
-
-  f32x4 acc_h[MTH];
-  const int64_t sb = (int64_t)(n * H + h) * DK * DV;
-  const int64_t cpb = ((int64_t)sg * N * H + n * H + h) * DK;
-#pragma unroll
-  for (int mt = 0; mt < MTH; ++mt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int dk = dkw + 16 * mt + acc_row0() + i, dv = dv0 + acc_col();
-      float v = 0.f;
-      if (MODE == 0) v = (mtile && dk == col0 + acc_col()) ? 1.f : 0.f;
-      else if (sg < CP - 1) v = a.dhend[(cpb + dk) * DV + dv];
-      else if (a.dhT) v = (a.layout == 0) ? a.dhT[sb + (int64_t)dk * DV + dv] : a.dhT[sb + (int64_t)dv * DK + dk];
-      acc_h[mt][i] = v;
-    }
-#pragma unroll
-  for (int mt = 0; mt < MTH; ++mt) store_acc_t2(sDH, sDHl, LDH, dkw + 16 * mt, 0, acc_h[mt]);
-
-  // this wave's operands of one chunk, read from its slot
-  struct Ops {
-    frag kf[KS];
-    frag wf[MTH][KS64];
-    f32x4 dl, z[MTH], ee;
-    float eL;
-  };
-  auto fetch = [&](int sl, Ops& o) {
-    const char* sp = ring + sl * SLOT;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) o.kf[ks] = *reinterpret_cast<const frag*>(sp + ((w * KS + ks) * 64 + l) * 16);
-#pragma unroll
-    for (int mt = 0; mt < MTH; ++mt)
-#pragma unroll
-      for (int ks = 0; ks < KS64; ++ks)
-        o.wf[mt][ks] = *reinterpret_cast<const frag*>(sp + OW + (((dkw / 16 + mt) * KS64 + ks) * 64 + l) * 16);
-    o.dl = *reinterpret_cast<const f32x4*>(sp + OD + w * 1024 + l * 16);
-#pragma unroll
-    for (int mt = 0; mt < MTH; ++mt) o.z[mt] = *reinterpret_cast<const f32x4*>(sp + OZ + (dkw / 16 + mt) * 1024 + l * 16);
-    const float* gs = reinterpret_cast<const float*>(sp + OG);
-    o.ee = *reinterpret_cast<const f32x4*>(gs + 64 + rw + acc_row0());
-    o.eL = gs[63];
-  };
-  // step j: chunk nc - 1 - j from o; reads the next chunk's operands into on
-  // right after the second barrier, so their LDS latency hides under the update
-  auto step = [&](int j, Ops& o, Ops& on) {
-    const int c = nc - 1 - j;
-    const int64_t ch = chb + c;
-    if constexpr (MODE != 0) {
-      T* db = (T*)a.dhs + ch * DK * DV;
-#pragma unroll
-      for (int mt = 0; mt < MTH; ++mt) store_acc4(db + acc_off(dkw / 16 + mt, dv0 / 16, DV), acc_h[mt]);
-    }
-    GDR_SYNC();  // dh^T complete; last chunk's readers of dDelta^T are done
-    // dDelta = E (K dh) + scale P^T dO, rows 16w
-    f32x4 acc_d = zero4();
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      acc_d = Mma<T>::mma(o.kf[ks], frag_rowk(sDH, LDH, 0, ks * KW), acc_d);
-      acc_d = Mma<T>::mma(o.kf[ks], frag_rowk(sDHl, LDH, 0, ks * KW), acc_d);
-    }
-    acc_d = acc_d * o.ee + (mtile ? zero4() : o.dl);
-    if constexpr (MODE != 0) store_acc4((T*)a.dD + ch * 64 * DV + acc_off(w, dv0 / 16, DV), acc_d);
-    store_acc_t2(sDD, sDDl, LDD, rw, 0, -acc_d);
-    GDR_SYNC();  // -dDelta^T complete; all readers of dh^T are done; the next slot is loaded
-    if (j + 1 < nc) fetch((j + 1) % R, on);
-    // dh <- e^{gamma_L} dh + scale Qg^T dO - W^T dDelta
-#pragma unroll
-    for (int mt = 0; mt < MTH; ++mt) acc_h[mt] = acc_h[mt] * o.eL + (mtile ? zero4() : o.z[mt]);
-#pragma unroll
-    for (int ks = 0; ks < KS64; ++ks) {
-      const frag bd = frag_rowk(sDD, LDD, 0, ks * KW);
-      const frag bdl = frag_rowk(sDDl, LDD, 0, ks * KW);
-#pragma unroll
-      for (int mt = 0; mt < MTH; ++mt) {
-        acc_h[mt] = Mma<T>::mma(o.wf[mt][ks], bd, acc_h[mt]);
-        acc_h[mt] = Mma<T>::mma(o.wf[mt][ks], bdl, acc_h[mt]);
-      }
-    }
-#pragma unroll
-    for (int mt = 0; mt < MTH; ++mt) store_acc_t2(sDH, sDHl, LDH, dkw + 16 * mt, 0, acc_h[mt]);
-  };
-  if (nc > 0) {
-    Ops op[2];
-    GDR_SYNC();  // slot 0 complete
-    fetch(0, op[0]);
-    int j = 0;
-    for (; j + 2 <= nc; j += 2) {
-      step(j, op[0], op[1]);
-      step(j + 1, op[1], op[0]);
-    }
-    if (j < nc) step(j, op[0], op[1]);
-  }
-  if (MODE == 0) {
-#pragma unroll
-    for (int mt = 0; mt < MTH; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int dk = dkw + 16 * mt + acc_row0() + i;
-        a.summ[(cpb + dk) * (DK + DV) + col0 + acc_col()] = acc_h[mt][i];
-      }
-  } else if (a.dh0 && sg == 0) {
-#pragma unroll
-    for (int mt = 0; mt < MTH; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int dk = dkw + 16 * mt + acc_row0() + i, dv = dv0 + acc_col();
-        if (a.layout == 0) a.dh0[sb + (int64_t)dk * DV + dv] = acc_h[mt][i];
-        else a.dh0[sb + (int64_t)dv * DK + dk] = acc_h[mt][i];
-      }
-  }
-}
-
 // value columns per phase-1 step of k_grad (keeps its LDS at two workgroups
 // per compute unit)
 #define GRAD_DVB 32
@@ -737,7 +502,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
         f32x4 y;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int s = r0 + i, dvl = 16 * nt + acc_col();
+          const int s = r0 + i;
           const float x = aVb[nt][i];
           y[i] = sb[s] * x;
         }
@@ -1038,25 +803,8 @@ static hipError_t launch_scan_bwd_t(ScanBwdArgs a, int dvt, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int DK, int MODE>
-static hipError_t launch_scan_bwd_p(ScanBwdArgs a, hipStream_t st) {
-  const int units = a.geo.N * a.geo.cp * a.geo.H;
-  a.ntiles = ((MODE == 0 ? DK : 0) + a.DV) / 16;
-  const int grid = 8 * ((units + 7) / 8) * a.ntiles;
-  if (units == 0) return hipSuccess;
-  const int nkf = 64 * DK / 512;
-  const size_t sm = (size_t)3 * (2 * nkf * 1024 + 4 * 1024 + (DK / 16) * 1024 + 512);
-  hipError_t e = hipFuncSetAttribute((const void*)k_scan_bwd_p<DK, MODE>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_scan_bwd_p<DK, MODE>), dim3(grid), dim3(64 * (4 + SCAN_PRODUCERS)), sm, st, a);
-  return hipGetLastError();
-}
-
 template <typename T, int DK>
 static hipError_t launch_scan_bwd_m(const ScanBwdArgs& a, int dvt, int mode, hipStream_t st) {
-  // bf16 operands at 16-column tiles: the producer-wave variant
-  if constexpr (sizeof(T) == 2)
-    if (dvt == 16) return mode == 0 ? launch_scan_bwd_p<DK, 0>(a, st) : launch_scan_bwd_p<DK, 1>(a, st);
   return mode == 0 ? launch_scan_bwd_t<T, DK, 0>(a, dvt, st) : launch_scan_bwd_t<T, DK, 1>(a, dvt, st);
 }
 

@@ -484,15 +484,6 @@ __device__ __forceinline__ bool unit_of(int b, int units, int ntiles, int& p, in
   return p < units;
 }
 
-// s_waitcnt on the vector-memory counter alone: wait until at most N vector
-// memory operations of this wave are outstanding (gfx9 encoding: vmcnt in
-// bits 3:0 and 15:14; expcnt and lgkmcnt at their maxima, i.e. not waited on)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 // ---------------------------------------------------------------------------
 // Workgroup barrier of every kernel.  The race-test build of the library
 // (compiled with GDR_DEBUG_DELAY) puts chosen waves to sleep after a
@@ -500,9 +491,6 @@ __device__ __forceinline__ void wait_vmcnt() {
 // data another wave still needs, without a barrier in between, then sees
 // different data and the results change.  The sleeps change no arithmetic,
 // so that build's outputs with and without delays must be bitwise equal.
-// GDR_BARRIER_ONLY is the hardware barrier without the memory fence, for a
-// wave whose only memory operations are global -> LDS loads whose completion
-// it tracks itself (the fence would wait for all of them).
 #ifdef GDR_DEBUG_DELAY
 struct DelayCfg {
   int wave;    // wave to delay, -1: every wave
@@ -525,14 +513,8 @@ __device__ __forceinline__ void debug_delay() {
     __syncthreads();        \
     ::gdr::debug_delay();   \
   } while (0)
-#define GDR_BARRIER_ONLY()           \
-  do {                               \
-    __builtin_amdgcn_s_barrier();    \
-    ::gdr::debug_delay();            \
-  } while (0)
 #else
 #define GDR_SYNC() __syncthreads()
-#define GDR_BARRIER_ONLY() __builtin_amdgcn_s_barrier()
 #endif
 
 }  // namespace gdr
