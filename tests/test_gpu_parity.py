@@ -335,3 +335,57 @@ def test_parity_full_size_long_context_cp8_both_snapshot_dtypes():
     for hs in ("f32", "f16"):
         say("[case] h_store %s" % hs)
         compare(w, run_gpu(w, inp, h_store=hs), ref, heads=heads)
+
+
+def _heads(inp, idx):
+    # the inputs of the given heads only ([B, T, H, ...] tensors and the
+    # [N, H, ...] states); cu_seqlens and other entries unchanged
+    out = {}
+    for k, v in inp.items():
+        if not isinstance(v, torch.Tensor) or k == "cu_seqlens":
+            out[k] = v
+        elif k in ("h0", "dhT"):
+            out[k] = v[:, idx].contiguous()
+        else:
+            out[k] = v[:, :, idx].contiguous()
+    return out
+
+
+def _pick(out, name, idx):
+    x = out[name]
+    return x[:, idx] if name in ("hT", "dh0") else x[:, :, idx]
+
+
+def test_heads_independent_bitwise_across_tile_widths():
+    # Heads are independent, and the scans' column tiles (16, 32 or 64
+    # columns, chosen from the number of (sequence, head) units) compute each
+    # column the same way, so every head's outputs must not depend on which
+    # other heads share the call -- bit for bit.  Workload 1 at full size
+    # (16-column tiles) against the same heads repeated 8 times (256 units:
+    # 64-column output tiles, 32-column reverse tiles), and head subsets of
+    # the packed and wide-value workloads.  A defect that touches a few
+    # hundred of millions of elements, too few for a normwise tolerance to
+    # see, shows here.
+    w = C[1]
+    say("[case] heads repeated x8 %s" % w.name)
+    inp = gin.generate(w)
+    base = run_gpu(w, inp)
+    rep = {k: (v.repeat(1, 8, *([1] * (v.dim() - 2))) if k in ("h0", "dhT") else
+               v.repeat(1, 1, 8, *([1] * (v.dim() - 3))))
+           if isinstance(v, torch.Tensor) and k != "cu_seqlens" else v for k, v in inp.items()}
+    big = run_gpu(w.replace(name="heads_x8", H=8 * w.H), rep)
+    for name in base:
+        if base[name] is None:
+            continue
+        for r in (0, 7):
+            got = _pick(big, name, list(range(r * w.H, (r + 1) * w.H)))
+            assert np.count_nonzero(got != base[name]) == 0, "%s copy %d" % (name, r)
+    del big, rep
+    for w, idx in [(C[2], [0, 5]), (C[4].replace(name="widev_T2048", B=1, T=2048), [3, 17])]:
+        say("[case] head subset %s %s" % (w.name, idx))
+        inp = gin.generate(w)
+        full = run_gpu(w, inp)
+        sub = run_gpu(w.replace(name=w.name + "_sub", H=len(idx)), _heads(inp, idx))
+        for name in full:
+            if full[name] is not None:
+                assert np.count_nonzero(_pick(full, name, idx) != sub[name]) == 0, "%s %s" % (w.name, name)
