@@ -52,8 +52,11 @@ def test_parity_small(case):
     compare(w, got, ref)
 
 
-def test_backward_with_saved_states_equals_recompute():
-    w = SMALL["cfg1_fixed_bf16_ragged"]
+@pytest.mark.parametrize("size", ["small", "full"])
+def test_backward_with_saved_states_equals_recompute(size):
+    # the snapshots the forward output scan writes and the ones the backward
+    # recomputes (snapshot-only scan) are the same bits, so every gradient is
+    w = SMALL["cfg1_fixed_bf16_ragged"] if size == "small" else C[1]
     say("[case] saved-vs-recompute %s" % w.name)
     inp = gin.generate(w)
     a = run_gpu(w, inp, saved=True)
