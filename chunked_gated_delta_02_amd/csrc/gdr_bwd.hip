@@ -150,6 +150,29 @@ __global__ __launch_bounds__(256) void k_scan_bwd(const ScanBwdArgs a) {
     }
   };
 
+  // L2 warming (16-bit operands).  The column tiles of a unit run in step
+  // and share its K and W^T fragments through their XCD's L2, but they
+  // request each chunk at the same moment, so every one of them waits for
+  // the HBM fill.  Each wave also touches one 1 KB fragment of its tile's
+  // share of the chunk WARM steps ahead (fragment jt + ntiles * wave of the
+  // 2 NKF K and W^T fragments; one dword per lane at a 16-byte stride reaches
+  // every line of it), so that the ring's loads of that chunk hit L2.  The
+  // value is consumed by an empty asm one step later, where the compiler's
+  // wait covers it.  At 8 or more tiles every shared fragment is warmed.
+  constexpr int WARM = 6;
+  constexpr int NKF = 64 * DK / 512;
+  float wcarry = 0.f;
+  auto warm = [&](int c) {
+    if constexpr (sizeof(T) == 2) {
+      asm volatile("" ::"v"(wcarry));
+      const int64_t ch = chb + max(c - WARM, 0);
+      const int q = (jt + a.ntiles * w) % (2 * NKF);
+      const T* base = q < NKF ? (const T*)a.Kf + ch * 64 * DK : (const T*)a.WTf + ch * DK * 64;
+      const int f = q < NKF ? q : q - NKF;
+      wcarry = *reinterpret_cast<const float*>(base + ((int64_t)f * 64 + lane_id()) * 8);
+    }
+  };
+
   // chunk c from stage o; with pf, the operands of chunk cn go to stage on
   auto process = [&](int c, Ops& o, int cn, Ops& on, bool pf) {
     const int64_t ch = chb + c;
@@ -190,6 +213,7 @@ __global__ __launch_bounds__(256) void k_scan_bwd(const ScanBwdArgs a) {
       // issue overlaps the MFMA chain instead of delaying the next barrier
       if (pf) {
         __builtin_amdgcn_sched_barrier(0);
+        if (ks == 0) warm(c);
 #pragma unroll
         for (int pc = 0; pc < 4; ++pc)
           if (pc * KS64 / 4 == ks) load_piece(cn, on, pc);
