@@ -159,11 +159,15 @@ __global__ __launch_bounds__(256) void k_scan_bwd(const ScanBwdArgs a) {
   // every line of it), so that the ring's loads of that chunk hit L2.  The
   // value is consumed by an empty asm one step later, where the compiler's
   // wait covers it.  At 8 or more tiles every shared fragment is warmed.
+  // 16-column tiles only: at 32 columns (a 2-stage ring, two waves per
+  // SIMD) the extra loads cost more than they save (B = 4, T = 8192, H = 32,
+  // DV = 256: 993 -> 1061 us), at 16 they save (B = 2, T = 4096, H = 16:
+  // 106.6 -> 102.1 us).
   constexpr int WARM = 6;
   constexpr int NKF = 64 * DK / 512;
   float wcarry = 0.f;
   auto warm = [&](int c) {
-    if constexpr (sizeof(T) == 2) {
+    if constexpr (sizeof(T) == 2 && DVT == 16) {
       asm volatile("" ::"v"(wcarry));
       const int64_t ch = chb + max(c - WARM, 0);
       const int q = (jt + a.ntiles * w) % (2 * NKF);
