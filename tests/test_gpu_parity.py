@@ -366,7 +366,7 @@ def test_heads_independent_bitwise_across_tile_widths():
     # other heads share the call -- bit for bit.  Workload 1 at full size
     # (16-column tiles) against the same heads repeated 8 times (256 units:
     # 64-column output tiles, 32-column reverse tiles), and head subsets of
-    # the packed and wide-value workloads.  A defect that touches a few
+    # the packed, wide-value and context-parallel workloads.  A defect that touches a few
     # hundred of millions of elements, too few for a normwise tolerance to
     # see, shows here.
     w = C[1]
@@ -384,7 +384,8 @@ def test_heads_independent_bitwise_across_tile_widths():
             got = _pick(big, name, list(range(r * w.H, (r + 1) * w.H)))
             assert np.count_nonzero(got != base[name]) == 0, "%s copy %d" % (name, r)
     del big, rep
-    for w, idx in [(C[2], [0, 5]), (C[4].replace(name="widev_T2048", B=1, T=2048), [3, 17])]:
+    for w, idx in [(C[2], [0, 5]), (C[4].replace(name="widev_T2048", B=1, T=2048), [3, 17]),
+                   (C[3].replace(name="cp8_T16384", T=16384), [2])]:
         say("[case] head subset %s %s" % (w.name, idx))
         inp = gin.generate(w)
         full = run_gpu(w, inp)
