@@ -305,7 +305,7 @@ def main():
                    args.calibrate_copy_mib or 256, 1)
         return
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(asked for --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import torch

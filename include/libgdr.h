@@ -57,7 +57,7 @@ extern "C" {
 typedef enum {
   GDR_OK = 0,
   GDR_ERR_INVALID_ARG = 1, /* bad dimension, null required pointer, misalignment */
-  GDR_ERR_UNSUPPORTED = 2, /* valid request outside what this build implements  */
+  GDR_ERR_UNSUPPORTED = 2, /* valid request outside what the library implements */
   GDR_ERR_WORKSPACE = 3,   /* workspace pointer null or smaller than required    */
   GDR_ERR_HIP = 4          /* a HIP launch failed                                */
 } gdr_status;
