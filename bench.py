@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true",
+                    help="skip the MFMA / bandwidth microbenchmarks (box-measured peaks)")
     ap.add_argument("--h-store", choices=("f32", "f16", "bf16"), default=None,
                     help="snapshot dtype (default: the workload's)")
     ap.add_argument("--flush-mib", type=int, default=512,
@@ -197,6 +199,103 @@ class Hip:
         self.lib.hipEventDestroy(ev)
 
 
+def metric_name(w, B, T, H, K, V):
+    """The metric string of the workload that ran: the headline workload's is
+    "GDR fwd+bwd tokens/s & TFLOPS (% bf16 MFMA peak), B=2 T=4096 H=16 D=128"."""
+    dims = "D=%d" % K if K == V else "DK=%d DV=%d" % (K, V)
+    if w.varlen:
+        shape = "N=%d varlen T=%d H=%d %s" % (w.n_seqs or len(w.lengths or []), T, H, dims)
+    else:
+        shape = "B=%d T=%d H=%d %s" % (B, T, H, dims)
+    extra = ""
+    if w.cp_segments > 1:
+        extra += " cp=%d" % w.cp_segments
+    if w.h_store != "f32":
+        extra += " h_store=%s" % w.h_store
+    prec = "bf16" if w.io_dtype == "bf16" else "fp32"
+    return "GDR fwd+bwd tokens/s & TFLOPS (%% %s MFMA peak), %s%s" % (prec, shape, extra)
+
+
+def direction_bytes(mode, NT, NP, K, V, e, n_states):
+    """Algorithmic HBM bytes of one direction: the operator's per-token
+    inputs read and outputs written once, plus its per-(sequence, head) fp32
+    states (h0 / h_T forward; h0, dh_T / dh0 backward)."""
+    if mode == "fwd":
+        per = 2 * K * e + 2 * V * e + 8
+    else:
+        per = (2 * K * e + 2 * V * e + 8) + (2 * K * e + V * e + 8)
+    return NT * per + n_states * NP * K * V * 4
+
+
+class Probe:
+    """Box-measured ceilings from libgdr_probe.so: dense bf16 MFMA rate and
+    streaming read / copy bandwidth, each timed with HIP events."""
+
+    def __init__(self, hip, torch, dev, stream):
+        path = os.path.join(ROOT, "chunked_gated_delta_02_amd", "libgdr_probe.so")
+        if not os.path.exists(path):
+            raise RuntimeError("%s is not built" % path)
+        self.lib = ctypes.CDLL(path)
+        L = self.lib
+        L.gdr_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                          ctypes.c_size_t, ctypes.c_void_p]
+        L.gdr_probe_mfma_bf16_flops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        L.gdr_probe_mfma_bf16_flops.restype = ctypes.c_double
+        L.gdr_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
+                                     ctypes.c_size_t, ctypes.c_void_p]
+        L.gdr_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                     ctypes.c_void_p]
+        self.hip, self.torch, self.dev, self.stream = hip, torch, dev, stream
+
+    def _time(self, fn, reps=5):
+        a, b = self.hip.event(), self.hip.event()
+        fn()
+        best = None
+        for _ in range(reps):
+            self.hip.record(a, self.stream)
+            rc = fn()
+            self.hip.record(b, self.stream)
+            if rc != 0:
+                raise RuntimeError("probe launch failed: %d" % rc)
+            self.torch.cuda.synchronize()
+            ms = self.hip.elapsed_ms(a, b)
+            best = ms if best is None else min(best, ms)
+        self.hip.destroy(a)
+        self.hip.destroy(b)
+        return best
+
+    def measure(self):
+        torch = self.torch
+        blocks, iters = 256 * 8, 4096
+        out = torch.empty(blocks * 256, dtype=torch.float32, device=self.dev)
+        rates = {}
+        for shape in (16, 32):
+            ms = self._time(lambda: self.lib.gdr_probe_mfma_bf16(shape, blocks, iters, out.data_ptr(),
+                                                                 out.numel(), self.stream))
+            rates[shape] = self.lib.gdr_probe_mfma_bf16_flops(shape, blocks, iters) / (ms * 1e-3)
+        mfma = max(rates.values())
+        nbytes = 2 << 30
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=self.dev)
+        dst = torch.empty_like(src)
+        rb = 256 * 16
+        part = torch.empty(rb * 256, dtype=torch.float32, device=self.dev)
+        ms_r = self._time(lambda: self.lib.gdr_probe_read(src.data_ptr(), nbytes, rb, part.data_ptr(),
+                                                          part.numel(), self.stream))
+        ms_c = self._time(lambda: self.lib.gdr_probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, rb,
+                                                          self.stream))
+        del src, dst, part, out
+        return {"bf16_mfma_tflops": round(mfma / 1e12, 1),
+                "bf16_mfma_tflops_16x16x32": round(rates[16] / 1e12, 1),
+                "bf16_mfma_tflops_32x32x16": round(rates[32] / 1e12, 1),
+                "hbm_read_GBps": round(nbytes / (ms_r * 1e-3) / 1e9, 1),
+                "hbm_copy_GBps": round(2 * nbytes / (ms_c * 1e-3) / 1e9, 1),
+                "method": "libgdr_probe.so: %d workgroups x 4 waves x %d rounds of 8 independent "
+                          "v_mfma_f32_16x16x32_bf16 or 4 of v_mfma_f32_32x32x16_bf16 (the faster "
+                          "counts); 2 GiB streaming read and copy with 16-byte "
+                          "accesses (copy counts read + write); best of 5 launches, HIP events"
+                          % (blocks, iters)}
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for f in sorted(os.listdir(os.path.join(ROOT, "chunked_gated_delta_02_amd", "csrc"))):
@@ -267,14 +366,19 @@ def cpu_baseline(w, inp, target_s):
     threads = oracle.max_threads()
     H = w.H
 
+    split = [0.0, 0.0]   # oracle seconds in the forward and backward calls
+
     def run(nh):
         sel = lambda t: t[:, :, :nh].double().numpy()
         q, k, v, beta, g, do = (sel(inp[n]) for n in ("q", "k", "v", "beta", "g", "do"))
         dhT = None if inp["dhT"] is None else inp["dhT"][:, :nh].double().numpy()
         t0 = time.perf_counter()
         oracle.fwd(q, k, v, beta, g, layout=w.layout)
+        t1 = time.perf_counter()
         oracle.bwd(q, k, v, beta, g, do, dhT=dhT, layout=w.layout)
-        return time.perf_counter() - t0
+        t2 = time.perf_counter()
+        split[0], split[1] = t1 - t0, t2 - t1
+        return t2 - t0
 
     # calibrate with as many heads as threads can take in one wave of pairs,
     # then grow the head subset (and, if the whole workload is quicker than
@@ -287,14 +391,21 @@ def cpu_baseline(w, inp, target_s):
     reps = 1
     if nh2 > nh:
         nh, t = nh2, run(nh2)
+    tf, tb = split
     if nh == H and t < target_s / 2:
         reps = max(1, int(target_s / t))
-        t = sum(run(nh) for _ in range(reps))
+        t, tf, tb = 0.0, 0.0, 0.0
+        for _ in range(reps):
+            t += run(nh)
+            tf += split[0]
+            tb += split[1]
     tokens = reps * w.B * w.T * nh / H
     return {"value": tokens / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "fwd_tokens_per_s": tokens / tf, "bwd_tokens_per_s": tokens / tb,
             "sample": "fp64 oracle forward+backward on %d of %d heads of all %d sequences "
-                      "(%d tokens x %d heads), %d repetition(s), %.1f s wall; tokens/s counts "
-                      "full tokens (all heads)" % (nh, H, w.B, w.B * w.T, nh, reps, t)}
+                      "(%d tokens x %d heads), %d repetition(s), %.1f s wall (forward %.1f s, "
+                      "backward %.1f s, timed separately); tokens/s counts full tokens (all heads)"
+                      % (nh, H, w.B, w.B * w.T, nh, reps, t, tf, tb)}
 
 
 def main():
@@ -368,17 +479,24 @@ def main():
     # those markers add small gaps, so the step time comes from the first.
     flush = torch.empty(args.flush_mib * (1 << 18), dtype=torch.float32, device=dev) if args.flush_mib else None
     evs = [[[hip.event() for _ in range(2 * nk)] for _ in range(2)] for _ in range(args.steps)]
-    sev = [(hip.event(), hip.event()) for _ in range(args.steps)]
+    # per step: start, end of forward (= start of backward), end
+    sev = [(hip.event(), hip.event(), hip.event()) for _ in range(args.steps)]
+    sevb = [(hip.event(), hip.event(), hip.event()) for _ in range(args.steps)]
     sev2 = [(hip.event(), hip.event()) for _ in range(args.steps)]
+
+    def timed_pass(evl):
+        for s in range(args.steps):
+            if flush is not None:
+                flush.fill_(float(s))
+            hip.record(evl[s][0], stream)
+            fwd()
+            hip.record(evl[s][1], stream)
+            bwd()
+            hip.record(evl[s][2], stream)
+
     torch.cuda.synchronize()
     t_host0 = time.perf_counter()
-    for s in range(args.steps):
-        if flush is not None:
-            flush.fill_(float(s))
-        hip.record(sev[s][0], stream)
-        fwd()
-        bwd()
-        hip.record(sev[s][1], stream)
+    timed_pass(sev)          # pass A: the K timed steps of the result
     torch.cuda.synchronize()
     t_host1 = time.perf_counter()
     for s in range(args.steps):
@@ -391,9 +509,18 @@ def main():
         bwd()
         hip.record(sev2[s][1], stream)
     _lib.gdr_set_kernel_timers(None)
+    timed_pass(sevb)         # pass B: the same steps again, after the marker pass
     torch.cuda.synchronize()
-    ms_step = sum(hip.elapsed_ms(a, b) for a, b in sev) / args.steps
+
+    def split_ms(evl):
+        return ([hip.elapsed_ms(a, c) for a, _, c in evl], [hip.elapsed_ms(a, b) for a, b, _ in evl],
+                [hip.elapsed_ms(b, c) for _, b, c in evl])
+
+    stepA, fwdA, bwdA = split_ms(sev)
+    stepB, fwdB, bwdB = split_ms(sevb)
+    ms_step = sum(stepA) / args.steps
     ms_step_timed = sum(hip.elapsed_ms(a, b) for a, b in sev2) / args.steps
+    med = lambda xs: sorted(xs)[len(xs) // 2] if len(xs) % 2 else 0.5 * sum(sorted(xs)[len(xs) // 2 - 1:len(xs) // 2 + 1])
     if args.calibrate_copy_mib:
         # scale reference for --pmc byte counters: fp32 elementwise multiply by
         # one, reading and writing calibrate_copy_mib MiB once each
@@ -420,10 +547,14 @@ def main():
         for ph in row:
             for e in ph:
                 hip.destroy(e)
-    for a_, b_ in sev + sev2:
-        hip.destroy(a_)
-        hip.destroy(b_)
+    for evl in (sev, sevb, sev2):
+        for tup in evl:
+            for e_ in tup:
+                hip.destroy(e_)
     del flush
+    peaks = None
+    if not args.no_probe:
+        peaks = Probe(hip, torch, dev, stream).measure()
 
     tokens = B * T
     NT = B * T * H
@@ -463,10 +594,26 @@ def main():
     roof["algorithmic_flops"] = int(fl)
     roof["traffic"] = measured_traffic(kname + "_" + phase, w.name)
 
-    fwd_ms = sum(v for k2, v in per.items() if k2.startswith("fwd."))
-    bwd_ms = sum(v for k2, v in per.items() if k2.startswith("bwd."))
+    fwd_ms = med(fwdA + fwdB)
+    bwd_ms = med(bwdA + bwdB)
+    nst_f = (h0 is not None) + 1                     # h0 read, h_T written
+    nst_b = (h0 is not None) + (dhT is not None) + 1  # h0, dh_T read, dh0 written
+    directions = {}
+    for mode, ms, fl_, ns in (("fwd", fwd_ms, fl_f, nst_f), ("bwd", bwd_ms, fl_b, nst_b)):
+        byt_d = direction_bytes(mode, NT, NP, K, V, e, ns)
+        directions[mode] = {
+            "median_ms": round(ms, 4),
+            "tflops": round(fl_ / (ms * 1e-3) / 1e12, 2),
+            "frac_bf16_peak": round(fl_ / (ms * 1e-3) / peak, 4),
+            "algorithmic_bytes": int(byt_d),
+            "algorithmic_GBps": round(byt_d / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(byt_d / (ms * 1e-3) / PEAK_HBM, 4),
+            "kernels_sum_ms": round(sum(v for k2, v in per.items() if k2.startswith(mode + ".")), 4)}
+        if peaks:
+            directions[mode]["frac_measured_mfma"] = round(fl_ / (ms * 1e-3) / (peaks["bf16_mfma_tflops"] * 1e12), 4)
+            directions[mode]["frac_measured_hbm"] = round(byt_d / (ms * 1e-3) / (peaks["hbm_read_GBps"] * 1e9), 4)
     res = {
-        "metric": "GDR fwd+bwd tokens/s & TFLOPS (% bf16 MFMA peak), B=2 T=4096 H=16 D=128",
+        "metric": metric_name(w, B, T, H, K, V),
         "value": round(tokens / (ms_step * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -488,11 +635,19 @@ def main():
         "frac_bf16_peak": round((fl_f + fl_b) / (ms_step * 1e-3) / PEAK_BF16_FLOPS, 4),
         "fwd_ms": round(fwd_ms, 4),
         "bwd_ms": round(bwd_ms, 4),
+        "directions": directions,
+        "protocol": {"warmup_steps": args.warmup, "timed_steps_per_pass": args.steps, "passes": 2,
+                     "value_from": "mean of pass A",
+                     "median_ms_per_step": round(med(stepA + stepB), 4),
+                     "pass_median_ms_per_step": [round(med(stepA), 4), round(med(stepB), 4)],
+                     "between_passes": "the per-kernel marker pass",
+                     "cache_flush_mib": args.flush_mib},
         "host_wall_ms_per_step": round((t_host1 - t_host0) * 1e3 / args.steps, 4),
         "ms_per_step_with_kernel_timers": round(ms_step_timed, 4),
         "cache_flush_mib": args.flush_mib,
         "kernels": kernels,
         "roofline": roof,
+        "peaks_measured": peaks,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -23,6 +23,12 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libgdr.so")
 DELAY_LIB = os.path.join(HERE, "libgdr_delay.so")
+# device code without kernels: exempt from the check that every .hip file
+# compiled kernels
+NO_KERNEL_SOURCES = set()
+# measurement probes (peak MFMA rate, streaming bandwidth): their own library
+PROBE_LIB = os.path.join(HERE, "libgdr_probe.so")
+PROBE_SOURCES = ["gdr_probe.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -51,7 +57,7 @@ def _compile(src: str, verbose: bool, delay: bool = False) -> str:
 def _check_resources(src: str, remarks: str) -> None:
     names = re.findall(r"Function Name: (\S+)", remarks)
     vgprs = [int(x) for x in re.findall(r"VGPRs: (\d+)", remarks)]
-    if src.endswith(".hip"):
+    if src.endswith(".hip") and src not in NO_KERNEL_SOURCES:
         if not names:
             raise RuntimeError("no kernels were compiled for %s (target dropped?)" % src)
         for n, v in zip(names, vgprs):
@@ -77,14 +83,18 @@ def _link(objs, lib: str) -> None:
 
 
 def build(verbose: bool = False, delay: bool = True) -> str:
-    """Build libgdr.so and (delay=True) the race-test build libgdr_delay.so."""
+    """Build libgdr.so, the probe library libgdr_probe.so and (delay=True)
+    the race-test build libgdr_delay.so."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    jobs = [(s, False) for s in SOURCES] + ([(s, True) for s in SOURCES] if delay else [])
+    jobs = ([(s, False) for s in SOURCES] + [(s, False) for s in PROBE_SOURCES] +
+            ([(s, True) for s in SOURCES] if delay else []))
     with cf.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
         objs = list(ex.map(lambda j: _compile(j[0], verbose, j[1]), jobs))
-    _link(objs[:len(SOURCES)], LIB)
+    n, m = len(SOURCES), len(PROBE_SOURCES)
+    _link(objs[:n], LIB)
+    _link(objs[n:n + m], PROBE_LIB)
     if delay:
-        _link(objs[len(SOURCES):], DELAY_LIB)
+        _link(objs[n + m:], DELAY_LIB)
     return LIB
 
 

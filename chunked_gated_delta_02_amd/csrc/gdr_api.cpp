@@ -60,7 +60,14 @@ gdr_status check_problem(const gdr_problem* p) {
   if (p->cp_segments < 1) { set_err("cp_segments must be >= 1 (got %d)", p->cp_segments); return GDR_ERR_INVALID_ARG; }
   if (p->cp_segments > 1024) { set_err("cp_segments must be <= 1024 (got %d)", p->cp_segments); return GDR_ERR_UNSUPPORTED; }
   const double tokens = (double)p->batch * p->seqlen;
-  if (tokens * p->heads * (p->dv > p->dk ? p->dv : p->dk) > 4.0e12) { set_err("problem too large"); return GDR_ERR_UNSUPPORTED; }
+  const int dmax = p->dv > p->dk ? p->dv : p->dk;
+  if (tokens * p->heads * dmax > 4.0e12) { set_err("problem too large"); return GDR_ERR_UNSUPPORTED; }
+  // the kernels address one chunk (64 token rows of H heads) of a [B, T, H, D]
+  // tensor through a raw buffer whose range and offsets are 32-bit byte counts
+  if (64.0 * p->heads * dmax * (double)elt(p->io_dtype) > 2147483647.0) {
+    set_err("64 x heads x max(dk, dv) x element size must stay below 2^31 bytes (heads %d, d %d)", p->heads, dmax);
+    return GDR_ERR_UNSUPPORTED;
+  }
   return GDR_OK;
 }
 

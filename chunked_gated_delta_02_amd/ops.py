@@ -51,6 +51,20 @@ def _ptr(t: Optional[torch.Tensor]) -> int:
 
 
 def _check_tensors(q, k, v, beta, g, cu_seqlens, extra=()):
+    # shapes first: the kernels take B, T and H from q and address every
+    # [B, T, H, ...] tensor with them, so a shorter v (or dO) would be read
+    # past its end
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k must be [B, T, H, DK] and v [B, T, H, DV]")
+    if k.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q and k must match in shape and dtype; v must match their dtype")
+    if v.shape[:3] != q.shape[:3]:
+        raise ValueError("v must be [B, T, H, DV] with the B, T, H of q (got %s vs %s)"
+                         % (tuple(v.shape), tuple(q.shape)))
+    if beta.dtype != torch.float32 or g.dtype != torch.float32:
+        raise ValueError("beta and g must be float32")
+    if beta.shape != q.shape[:3] or g.shape != q.shape[:3]:
+        raise ValueError("beta and g must be [B, T, H]")
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("libgdr runs on the GPU: tensors must be on a cuda device")
@@ -61,12 +75,6 @@ def _check_tensors(q, k, v, beta, g, cu_seqlens, extra=()):
             raise ValueError("%s is on %s, expected %s" % (name, t.device, dev))
         if not t.is_contiguous():
             raise ValueError("%s must be contiguous" % name)
-    if k.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("q and k must match in shape and dtype; v must match their dtype")
-    if beta.dtype != torch.float32 or g.dtype != torch.float32:
-        raise ValueError("beta and g must be float32")
-    if beta.shape != q.shape[:3] or g.shape != q.shape[:3]:
-        raise ValueError("beta and g must be [B, T, H]")
     if cu_seqlens is not None:
         if cu_seqlens.dtype != torch.int32 or cu_seqlens.device != dev or not cu_seqlens.is_contiguous():
             raise ValueError("cu_seqlens must be a contiguous int32 tensor on the same device")
@@ -112,9 +120,9 @@ def chunk_gdr_bwd(q, k, v, beta, g, do, cu_seqlens=None, h0=None, dhT=None, h_sa
                   layout="KV", scale=None, h_store="f32", need_dh0=True, cp_segments=1, need=GRADS):
     """Backward.  Returns dict(dq, dk, dv, dbeta, dg, dh0); the gradients not
     named in ``need`` (and dh0 unless ``need_dh0``) are None and not written."""
-    _check_tensors(q, k, v, beta, g, cu_seqlens, [("h0", h0), ("do", do), ("dhT", dhT), ("h_saved", h_saved)])
     if do.shape != v.shape or do.dtype != v.dtype:
         raise ValueError("do must match v in shape and dtype")
+    _check_tensors(q, k, v, beta, g, cu_seqlens, [("h0", h0), ("do", do), ("dhT", dhT), ("h_saved", h_saved)])
     p = make_problem(q, v, cu_seqlens, layout, scale, h_store, cp_segments)
     B, T, H, DK = q.shape
     DV = v.shape[-1]

@@ -12,6 +12,34 @@ from chunked_gated_delta_02_amd import ops
 from oracle import oracle
 
 TOL = {"f32": 1e-5, "bf16": 5e-3}
+# Element-wise bounds, checked beside the normwise one.  A normwise error over
+# a whole tensor cannot see a defect confined to a few rows (a few hundred
+# wrong values among millions), so every output is also held to
+#   emax = max|x - y| / max|y|                 (the rel_max of the FastVideo
+#          PR #1819 race study, "Results" table), and
+#   row  = max over rows r of max|x_r - y_r| / max(rms(y_r), 0.1 rms(y)),
+#          each element's error against the RMS magnitude of its own row,
+# with a row = one token-head vector of o, dq, dk, dv (length DK or DV), one
+# row of a state h_T / dh0, and 64 consecutive tokens of one head of dbeta /
+# dg (a chunk's worth: single elements of these scalar outputs are too noisy
+# to bound tightly).  The 0.1 rms floor keeps rows of near-zero reference
+# norm from dominating.  The limits are about 1.5x the largest value measured
+# over every parity workload of the GPU tests (full-size workloads 1-4
+# included) with the kernels as they stand; the bf16 rows are dominated by
+# the rounding of outputs and MFMA operands to 8 significant bits (output
+# rounding alone gives about 1.5e-2 of a row's RMS at 10^5 rows), the fp32
+# ones by accumulation order.
+_F32_EMAX, _F32_ROW = 1e-5, 6e-5
+EMAX_TOL = {
+    "f32": {n: _F32_EMAX for n in ("o", "hT", "dq", "dk", "dv", "dbeta", "dg", "dh0")},
+    "bf16": {"o": 6e-3, "hT": 1e-3, "dq": 7.5e-3, "dk": 6e-3, "dv": 9e-3, "dbeta": 6e-3, "dg": 8e-3,
+             "dh0": 1.5e-3},
+}
+ROW_TOL = {
+    "f32": {n: _F32_ROW for n in ("o", "hT", "dq", "dk", "dv", "dbeta", "dg", "dh0")},
+    "bf16": {"o": 2.5e-2, "hT": 4e-3, "dq": 6.5e-2, "dk": 9e-2, "dv": 7e-2, "dbeta": 6.5e-2, "dg": 7.5e-2,
+             "dh0": 1e-2},
+}
 OUTS_FWD = ("o", "hT")
 OUTS_BWD = ("dq", "dk", "dv", "dbeta", "dg", "dh0")
 
@@ -29,13 +57,53 @@ def rel(x, y) -> float:
     return float(d / n) if n > 0 else float(d)
 
 
+def rel_emax(x, y) -> float:
+    x = np.asarray(x, dtype=np.float64).ravel()
+    y = np.asarray(y, dtype=np.float64).ravel()
+    m = np.abs(y).max() if y.size else 0.0
+    d = np.abs(x - y).max() if y.size else 0.0
+    return float(d / m) if m > 0 else float(d)
+
+
+def _rows(name: str, a) -> np.ndarray:
+    """The rows of an output the row error is taken over: o, dq, dk, dv and
+    the states h_T, dh0 by their last axis; dbeta and dg ([B, T, H]) in
+    blocks of 64 consecutive tokens of one head (zero-padded at the end)."""
+    a = np.asarray(a, dtype=np.float64)
+    if name not in ("dbeta", "dg"):
+        return a.reshape(-1, a.shape[-1]) if a.size else a.reshape(0, 1)
+    a = np.moveaxis(a, -1, 1)                   # [B, H, T]
+    T = a.shape[-1]
+    pad = (-T) % 64
+    if pad:
+        a = np.concatenate([a, np.zeros(a.shape[:-1] + (pad,))], axis=-1)
+    return a.reshape(-1, 64) if a.size else a.reshape(0, 64)
+
+
+def rel_row(x, y, name: str) -> float:
+    """Largest element error relative to the RMS magnitude of its own row,
+    rows of near-zero RMS measured against 0.1 x the tensor's RMS."""
+    x = _rows(name, x)
+    y = _rows(name, y)
+    if y.size == 0:
+        return 0.0
+    ry = np.sqrt((y * y).mean(axis=1))
+    rms = float(np.sqrt((y * y).mean()))
+    d = np.abs(x - y).max(axis=1)
+    if rms == 0.0:
+        return float(d.max())
+    return float((d / np.maximum(ry, 0.1 * rms)).max())
+
+
 def to64(t):
     return None if t is None else t.detach().to("cpu").double().numpy()
 
 
-def run_gpu(w: gin.Workload, inp: dict, h_store=None, saved=True, device="cuda", cp_fwd=None, cp_bwd=None):
+def run_gpu(w: gin.Workload, inp: dict, h_store=None, saved=True, device="cuda", cp_fwd=None, cp_bwd=None,
+            keep_heads=None):
     """libgdr forward + backward; returns dict of fp64 NumPy arrays.  The
-    context-parallel segment counts default to the workload's."""
+    context-parallel segment counts default to the workload's.  With
+    `keep_heads`, only those heads of every output are copied back."""
     dev = {k: (v.to(device) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
     hs = h_store or w.h_store
     cp_fwd = w.cp_segments if cp_fwd is None else cp_fwd
@@ -53,9 +121,13 @@ def run_gpu(w: gin.Workload, inp: dict, h_store=None, saved=True, device="cuda",
                           cu_seqlens=dev["cu_seqlens"], h0=dev["h0"], dhT=dev["dhT"],
                           h_saved=h_saved, layout=w.layout, h_store=hs, cp_segments=cp_bwd)
     torch.cuda.synchronize()
-    out = dict(o=to64(o), hT=to64(hT))
-    out.update({k: to64(v) for k, v in r.items()})
-    return out
+    out = dict(o=o, hT=hT)
+    out.update(r)
+    if keep_heads is not None:
+        idx = torch.tensor(list(keep_heads), device=o.device)
+        out = {k: (None if v is None else
+                   v.index_select(1 if k in ("hT", "dh0") else 2, idx)) for k, v in out.items()}
+    return {k: to64(v) for k, v in out.items()}
 
 
 def run_oracle(w: gin.Workload, inp: dict, heads=None):
@@ -74,14 +146,29 @@ def run_oracle(w: gin.Workload, inp: dict, heads=None):
 
 
 def compare(w: gin.Workload, got: dict, ref: dict, heads=None, tol=None):
+    """Normwise, max-element and worst-row relative errors of every output
+    against the oracle; `heads` selects the heads `ref` was computed for
+    (None: `got` already holds exactly those)."""
     tol = tol if tol is not None else TOL[w.io_dtype]
-    errs = {}
+    etol, rtol = EMAX_TOL[w.io_dtype], ROW_TOL[w.io_dtype]
+    errs, emax, rows = {}, {}, {}
     for name in OUTS_FWD + OUTS_BWD:
         x = got[name]
         if heads is not None:
             x = x[:, heads] if name in ("hT", "dh0") else x[:, :, heads]
-        errs[name] = rel(x, ref[name])
+        y = ref[name]
+        errs[name] = rel(x, y)
+        emax[name] = rel_emax(x, y)
+        rows[name] = rel_row(x, y, name)
     say("[errors] %s: %s" % (w.name, " ".join("%s=%.2e" % kv for kv in errs.items())))
+    say("[errors-emax] %s: %s" % (w.name, " ".join("%s=%.2e" % kv for kv in emax.items())))
+    say("[errors-row] %s: %s" % (w.name, " ".join("%s=%.2e" % kv for kv in rows.items())))
     bad = {k: v for k, v in errs.items() if not (v <= tol)}
     assert not bad, "normwise error above %.0e: %s" % (tol, bad)
+    if etol is not None:
+        bad = {k: v for k, v in emax.items() if not (v <= etol[k])}
+        assert not bad, "max-element error above its limit: %s" % bad
+    if rtol is not None:
+        bad = {k: v for k, v in rows.items() if not (v <= rtol[k])}
+        assert not bad, "worst-row error above its limit: %s" % bad
     return errs

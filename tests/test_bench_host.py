@@ -58,3 +58,25 @@ def test_pmc_ingest_scales_by_the_copy_kernel_and_checks_the_sources(tmp_path, m
     # figures taken on other kernel sources are not reported
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "bbbb")
     assert bench.measured_traffic("grad_bwd", "wl") is None
+
+
+def test_metric_string_names_the_workload_that_ran():
+    from chunked_gated_delta_02_amd import inputs as gin
+    C = gin.CONFIGS
+    assert bench.metric_name(C[1], 2, 4096, 16, 128, 128) == \
+        "GDR fwd+bwd tokens/s & TFLOPS (% bf16 MFMA peak), B=2 T=4096 H=16 D=128"
+    assert bench.metric_name(C[4], 4, 8192, 32, 128, 256).endswith("B=4 T=8192 H=32 DK=128 DV=256")
+    assert bench.metric_name(C[3], 1, 65536, 8, 128, 128).endswith("B=1 T=65536 H=8 D=128 cp=8")
+    assert "N=8 varlen" in bench.metric_name(C[2], 1, 34000, 32, 128, 128)
+    assert "fp32 MFMA" in bench.metric_name(C[0], 1, 256, 2, 64, 64)
+    assert bench.metric_name(C[1].replace(h_store="f16"), 2, 4096, 16, 128, 128).endswith("h_store=f16")
+
+
+def test_direction_algorithmic_bytes():
+    # forward: q, k, v, beta, g read and o written (2 K e + 2 V e + 8 per
+    # token-head) plus h_T; backward: q, k, v, dO, beta, g read and dq, dk,
+    # dv, dbeta, dg written, plus dh_T read and dh0 written
+    nt, npairs = 2 * 4096 * 16, 32
+    state = npairs * 128 * 128 * 4
+    assert bench.direction_bytes("fwd", nt, npairs, 128, 128, 2, 1) == nt * (4 * 128 * 2 + 8) + state
+    assert bench.direction_bytes("bwd", nt, npairs, 128, 128, 2, 2) == nt * 1808 + 2 * state

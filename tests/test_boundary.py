@@ -93,11 +93,21 @@ def test_valid_problems(lib):
     (dict(io_dtype=_lib.GDR_F32, h_store_dtype=_lib.GDR_F16), _lib.GDR_ERR_UNSUPPORTED),
     (dict(layout=2), _lib.GDR_ERR_INVALID_ARG),
     (dict(cp_segments=0), _lib.GDR_ERR_INVALID_ARG),
+    # a chunk's rows of every head must stay addressable with 32-bit byte
+    # offsets: 64 x H x max(dk, dv) x element size < 2^31
+    (dict(io_dtype=_lib.GDR_F32, dv=512, heads=16384), _lib.GDR_ERR_UNSUPPORTED),
+    (dict(dv=512, heads=32768, seqlen=64), _lib.GDR_ERR_UNSUPPORTED),
 ])
 def test_invalid_problems(lib, kw, status):
     assert _lib.gdr_check(good(**kw)) == status
     assert _lib.gdr_fwd_workspace_bytes(good(**kw)) == 0
     assert _lib.last_error() != ""
+
+
+def test_largest_addressable_head_count(lib):
+    # 64 x 16383 x 512 x 4 bytes is just below 2^31
+    assert _lib.gdr_check(good(io_dtype=_lib.GDR_F32, dv=512, heads=16383, seqlen=64)) == _lib.GDR_OK
+    assert _lib.gdr_check(good(dv=512, heads=32767, seqlen=64)) == _lib.GDR_OK
 
 
 def test_null_problem(lib):

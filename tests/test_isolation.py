@@ -100,3 +100,26 @@ def test_cpu_tensors_are_refused_not_computed():
     beta = torch.zeros(B, T, H)
     with pytest.raises(ValueError, match="GPU"):
         ops.chunk_gdr_fwd(q, q.clone(), q.clone(), beta, beta.clone())
+
+
+def test_mismatched_value_shapes_are_refused_before_any_launch(monkeypatch):
+    # v (and dO) must share B, T and H with q: the kernels address them with
+    # q's sizes.  The checks run on the host, before the library is reached.
+    from chunked_gated_delta_02_amd import _lib, ops
+    calls = []
+    for name in ("gdr_chunk_fwd", "gdr_chunk_bwd", "gdr_check"):
+        monkeypatch.setattr(_lib, name, lambda *a, _n=name, **k: calls.append(_n))
+    B, T, H, D = 1, 8, 2, 64
+    q = torch.zeros(B, T, H, D, dtype=torch.bfloat16)
+    beta = torch.zeros(B, T, H)
+    for bad_v in (torch.zeros(B, T - 1, H, D, dtype=torch.bfloat16),
+                  torch.zeros(B, T, H - 1, D, dtype=torch.bfloat16),
+                  torch.zeros(B + 1, T, H, D, dtype=torch.bfloat16)):
+        with pytest.raises(ValueError, match="B, T, H"):
+            ops.chunk_gdr_fwd(q, q.clone(), bad_v, beta, beta.clone())
+        with pytest.raises(ValueError, match="B, T, H"):
+            ops.chunk_gdr_bwd(q, q.clone(), bad_v, beta, beta.clone(), bad_v.clone())
+    v = torch.zeros(B, T, H, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="do must match v"):
+        ops.chunk_gdr_bwd(q, q.clone(), v, beta, beta.clone(), v[:, :4].clone())
+    assert calls == []
