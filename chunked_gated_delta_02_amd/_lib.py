@@ -22,8 +22,10 @@ GDR_LAYOUT_KV, GDR_LAYOUT_VK = 0, 1
 
 # every function the header declares, for the export check
 EXPORTS = ("gdr_check", "gdr_fwd_workspace_bytes", "gdr_bwd_workspace_bytes", "gdr_h_saved_bytes",
-           "gdr_chunk_fwd", "gdr_chunk_bwd", "gdr_set_kernel_timers", "gdr_status_string",
-           "gdr_last_error", "gdr_version")
+           "gdr_chunk_fwd", "gdr_chunk_bwd", "gdr_chunk_fwd_noalloc", "gdr_set_kernel_timers",
+           "gdr_status_string", "gdr_last_error", "gdr_version")
+# size of the static workspace of gdr_chunk_fwd_noalloc (GDR_NOALLOC_SCRATCH_BYTES)
+GDR_NOALLOC_SCRATCH_BYTES = 64 << 20
 KERNELS = ("plan", "wy", "scan_fwd", "scan_bwd", "grad", "cp_scan_fwd", "cp_chain_fwd", "cp_scan_bwd",
            "cp_chain_bwd")
 
@@ -85,6 +87,8 @@ def _open(path: str):
         lib.gdr_chunk_bwd.argtypes = [P, vp, vp, vp, fp, fp, ip, fp, vp, vp, fp, vp, vp, vp, fp, fp, fp,
                                       vp, ctypes.c_size_t, vp]
         lib.gdr_chunk_bwd.restype = ctypes.c_int
+        lib.gdr_chunk_fwd_noalloc.argtypes = [P, vp, vp, vp, fp, fp, ip, fp, vp, fp, vp, vp]
+        lib.gdr_chunk_fwd_noalloc.restype = ctypes.c_int
         lib.gdr_set_kernel_timers.argtypes = [ctypes.c_void_p]
         lib.gdr_set_kernel_timers.restype = ctypes.c_int
         lib.gdr_status_string.argtypes = [ctypes.c_int]
@@ -168,6 +172,14 @@ def gdr_chunk_fwd(p, q, k, v, beta, g, cu_seqlens, h0, o, hT, h_saved, ws, ws_by
     """Raw call; all tensor arguments are integer device addresses (0 = NULL)."""
     st = _h().gdr_chunk_fwd(ctypes.byref(p), q, k, v, beta, g, cu_seqlens or None, h0 or None, o,
                               hT or None, h_saved or None, ws or None, ws_bytes, stream or None)
+    return _raise_on(st) if check else st
+
+
+def gdr_chunk_fwd_noalloc(p, q, k, v, beta, g, cu_seqlens, h0, o, hT, h_saved, stream, check=True) -> int:
+    """Raw call of the allocation-free forward (the library's static
+    workspace); all tensor arguments are integer device addresses (0 = NULL)."""
+    st = _h().gdr_chunk_fwd_noalloc(ctypes.byref(p), q, k, v, beta, g, cu_seqlens or None, h0 or None, o,
+                                      hT or None, h_saved or None, stream or None)
     return _raise_on(st) if check else st
 
 

@@ -23,16 +23,16 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libgdr.so")
 DELAY_LIB = os.path.join(HERE, "libgdr_delay.so")
-# device code without kernels: exempt from the check that every .hip file
-# compiled kernels
-NO_KERNEL_SOURCES = set()
+# device code without kernels (the static workspace of the allocation-free
+# entry point): exempt from the check that every .hip file compiled kernels
+NO_KERNEL_SOURCES = {"gdr_noalloc.hip"}
 # measurement probes (peak MFMA rate, streaming bandwidth): their own library
 PROBE_LIB = os.path.join(HERE, "libgdr_probe.so")
 PROBE_SOURCES = ["gdr_probe.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["gdr_fwd.hip", "gdr_bwd.hip", "gdr_api.cpp"]
+SOURCES = ["gdr_fwd.hip", "gdr_bwd.hip", "gdr_api.cpp", "gdr_noalloc.hip"]
 FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU instructions are kept off for all device code

@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstring>
 
+#include "gdr_host.h"
 #include "gdr_kernels.h"
 
 namespace {
@@ -188,33 +189,18 @@ char* align_ws(void* ws) { return (char*)(((uintptr_t)ws + 255) & ~(uintptr_t)25
 
 }  // namespace
 
-extern "C" {
+namespace gdr {
 
-gdr_status gdr_check(const gdr_problem* p) {
-  g_err[0] = 0;
-  return check_problem(p);
-}
+void set_error(const char* msg) { snprintf(g_err, sizeof(g_err), "%s", msg); }
 
-size_t gdr_fwd_workspace_bytes(const gdr_problem* p) {
-  if (check_problem(p) != GDR_OK) return 0;
-  return make_plan(p, 0, false).total;
-}
+size_t fwd_workspace_bytes(const gdr_problem* p) { return make_plan(p, 0, false).total; }
 
-size_t gdr_bwd_workspace_bytes(const gdr_problem* p, int have_h_saved) {
-  if (check_problem(p) != GDR_OK) return 0;
-  return make_plan(p, 1, !have_h_saved).total;
-}
-
-size_t gdr_h_saved_bytes(const gdr_problem* p) {
-  if (check_problem(p) != GDR_OK) return 0;
-  Plan pl = make_plan(p, 0, false);
-  return (size_t)pl.NCb * p->heads * p->dv * p->dk * pl.hsz;
-}
-
-gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
-                         const float* beta, const float* g, const int32_t* cu_seqlens,
-                         const float* h0, void* o, float* hT, void* h_saved, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+// The forward proper, on a caller-provided workspace (gdr_chunk_fwd) or the
+// library's static one (gdr_chunk_fwd_noalloc).
+gdr_status chunk_fwd_impl(const gdr_problem* p, const void* q, const void* k, const void* v,
+                          const float* beta, const float* g, const int32_t* cu_seqlens,
+                          const float* h0, void* o, float* hT, void* h_saved, void* workspace,
+                          size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
   gdr_status st = check_problem(p);
   if (st != GDR_OK) return st;
@@ -259,6 +245,39 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, con
   // mode 2 writes the snapshots to h_saved; mode 3 keeps none
   GDR_LAUNCH(GDR_KERNEL_SCAN_FWD, s, gdr::launch_scan_fwd(sa, pl.f32, p->h_store_dtype, p->dk, pick_dvt(units, p->dv, pl.f32, true), h_saved ? 2 : 3, s));
   return GDR_OK;
+}
+
+}  // namespace gdr
+
+extern "C" {
+
+gdr_status gdr_check(const gdr_problem* p) {
+  g_err[0] = 0;
+  return check_problem(p);
+}
+
+size_t gdr_fwd_workspace_bytes(const gdr_problem* p) {
+  if (check_problem(p) != GDR_OK) return 0;
+  return make_plan(p, 0, false).total;
+}
+
+size_t gdr_bwd_workspace_bytes(const gdr_problem* p, int have_h_saved) {
+  if (check_problem(p) != GDR_OK) return 0;
+  return make_plan(p, 1, !have_h_saved).total;
+}
+
+size_t gdr_h_saved_bytes(const gdr_problem* p) {
+  if (check_problem(p) != GDR_OK) return 0;
+  Plan pl = make_plan(p, 0, false);
+  return (size_t)pl.NCb * p->heads * p->dv * p->dk * pl.hsz;
+}
+
+gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
+                         const float* beta, const float* g, const int32_t* cu_seqlens,
+                         const float* h0, void* o, float* hT, void* h_saved, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return gdr::chunk_fwd_impl(p, q, k, v, beta, g, cu_seqlens, h0, o, hT, h_saved, workspace, workspace_bytes,
+                             stream);
 }
 
 gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, const void* v,

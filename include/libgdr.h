@@ -133,6 +133,22 @@ gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, con
                          void* dq, void* dk, void* dv, float* dbeta, float* dg, float* dh0,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the forward of
+ * gdr_chunk_fwd with no workspace argument.  It runs the same kernels on a
+ * static device array of the library, GDR_NOALLOC_SCRATCH_BYTES bytes on
+ * every GPU it runs on (kept until the process ends), and allocates nothing.
+ * Problems whose gdr_fwd_workspace_bytes() exceeds that size are refused
+ * with GDR_ERR_UNSUPPORTED before any launch.  The array is shared by every
+ * call on the same GPU: calls whose launches can overlap there (different
+ * streams with no ordering between them) race; calls ordered on one stream
+ * do not.  The stream must belong to the current device.  Arguments and
+ * outputs as in gdr_chunk_fwd. */
+#define GDR_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+gdr_status gdr_chunk_fwd_noalloc(const gdr_problem* p, const void* q, const void* k, const void* v,
+                                 const float* beta, const float* g, const int32_t* cu_seqlens,
+                                 const float* h0, void* o, float* hT, void* h_saved, void* stream);
+
 /* Diagnostics: per-kernel timing with caller-owned HIP events.
  * Kernel ids of the launches a forward / backward call makes: */
 enum {
