@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", choices=("gdr", "rmsnorm_bwd"), default="gdr",
+                    help="gdr: the gated delta rule step (default); rmsnorm_bwd: the fused RMSNorm "
+                         "backward sweep with its three dw reduction modes")
     ap.add_argument("--no-probe", action="store_true",
                     help="skip the MFMA / bandwidth microbenchmarks (box-measured peaks)")
     ap.add_argument("--h-store", choices=("f32", "f16", "bf16"), default=None,
@@ -408,8 +411,99 @@ def cpu_baseline(w, inp, target_s):
                       % (nh, H, w.B, w.B * w.T, nh, reps, t, tf, tb)}
 
 
+# The M x N points of the bf16 sweep on the quack PR #101 page ("Rmsnorm
+# backward fusing sum"): M 4k..65k rows, N 256..8k.
+RMSNORM_SWEEP = [(m, n) for n in (256, 512, 1024, 2048, 4096) for m in (4096, 8192, 16384, 32768, 65536)] + \
+    [(m, 8192) for m in (4096, 16384, 65536)]
+
+
+def bench_rmsnorm(args):
+    """Fused RMSNorm backward: every sweep point in the three dw reduction
+    modes, timed with HIP events (median of the timed launches, Infinity
+    Cache flushed between launches), as a fraction of HBM bandwidth; the cost
+    of determinism is the fixed-order time over the atomic one."""
+    import torch
+    from chunked_gated_delta_02_amd import _lib, rmsnorm
+    _lib.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    hip = Hip()
+    # inputs of the largest point, drawn on the device (seeded); smaller
+    # points use leading slices
+    gen = torch.Generator(device=dev).manual_seed(0)
+    mmax = max(m for m, _ in RMSNORM_SWEEP)
+    nmax = max(n for _, n in RMSNORM_SWEEP)
+    xs = torch.randn(mmax * nmax, generator=gen, device=dev).to(torch.bfloat16)
+    dys = torch.randn(mmax * nmax, generator=gen, device=dev).to(torch.bfloat16)
+    w = 1.0 + 0.1 * torch.randn(nmax, generator=gen, device=dev)
+    rstd = torch.rand(mmax, generator=gen, device=dev) + 0.5
+    flush = torch.empty(args.flush_mib * (1 << 18), dtype=torch.float32, device=dev) if args.flush_mib else None
+    steps = args.steps
+    points = []
+    for M, N in RMSNORM_SWEEP:
+        x = xs[:M * N].view(M, N)
+        dy = dys[:M * N].view(M, N)
+        dx = torch.empty_like(x)
+        dw = torch.zeros(N, dtype=torch.float32, device=dev)
+        row = {"M": M, "N": N}
+        for mode in ("fixed", "atomic", "separate"):
+            mcode = rmsnorm.MODES[mode]
+            ws = rmsnorm.workspace(M, N, mode, dev)
+            nb = 0 if ws is None else ws.numel()
+            P = lambda t: 0 if t is None else t.data_ptr()
+
+            def call():
+                _lib.gdr_rmsnorm_bwd(M, N, _lib.GDR_BF16, P(x), P(w[:N]), P(dy), P(rstd[:M]), 1e-6, P(dx),
+                                     P(dw), mcode, P(ws), nb, stream)
+
+            for _ in range(args.warmup):
+                call()
+            evs = [(hip.event(), hip.event()) for _ in range(steps)]
+            for a_, b_ in evs:
+                if flush is not None:
+                    flush.fill_(1.0)
+                hip.record(a_, stream)
+                call()
+                hip.record(b_, stream)
+            torch.cuda.synchronize()
+            ts = sorted(hip.elapsed_ms(a_, b_) for a_, b_ in evs)
+            for a_, b_ in evs:
+                hip.destroy(a_)
+                hip.destroy(b_)
+            row[mode + "_us"] = round(1e3 * ts[len(ts) // 2], 2)
+        byt = 3 * M * N * 2 + N * 4 * 2 + M * 4      # x, dy read, dx written (bf16); w, dw; rstd
+        row["algorithmic_bytes"] = byt
+        row["fixed_GBps"] = round(byt / (row["fixed_us"] * 1e-6) / 1e9, 1)
+        row["fixed_frac_hbm"] = round(byt / (row["fixed_us"] * 1e-6) / PEAK_HBM, 4)
+        row["determinism_cost"] = round(row["fixed_us"] / row["atomic_us"], 3)
+        row["fused_speedup_vs_separate"] = round(row["separate_us"] / row["fixed_us"], 3)
+        points.append(row)
+    import math
+    gm = lambda xs_: math.exp(sum(math.log(v) for v in xs_) / len(xs_))
+    big = max(points, key=lambda r: r["algorithmic_bytes"])
+    res = {"metric": "fused RMSNorm backward (bf16) time per call in three dw reduction modes",
+           "workload": "rmsnorm_bwd_bf16_sweep_M4096-65536_N256-8192",
+           "unit": "us", "steps": steps, "warmup": args.warmup, "cache_flush_mib": args.flush_mib,
+           "points": points,
+           "summary": {"geomean_determinism_cost_fixed_over_atomic": round(gm([r["determinism_cost"] for r in points]), 3),
+                       "geomean_fused_speedup_fixed_vs_separate": round(gm([r["fused_speedup_vs_separate"] for r in points]), 3),
+                       "largest_point": {"M": big["M"], "N": big["N"], "fixed_us": big["fixed_us"],
+                                         "fixed_frac_hbm": big["fixed_frac_hbm"]}},
+           "roofline": {"bound": "hbm", "achieved": big["fixed_GBps"], "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                        "frac": big["fixed_frac_hbm"], "kernel": "k_rmsnorm_bwd (fixed-order mode)",
+                        "traffic": None}}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
+    if args.workload == "rmsnorm_bwd":
+        if args.gpus != 1:
+            print("bench.py runs on one GPU only (asked for --gpus %d)" % args.gpus, file=sys.stderr)
+            sys.exit(2)
+        bench_rmsnorm(args)
+        return
     if args.ingest_pmc:
         from chunked_gated_delta_02_amd import inputs as gin
         ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], gin.CONFIGS[args.config].name,

@@ -24,6 +24,9 @@ GDR_LAYOUT_KV, GDR_LAYOUT_VK = 0, 1
 EXPORTS = ("gdr_check", "gdr_fwd_workspace_bytes", "gdr_bwd_workspace_bytes", "gdr_h_saved_bytes",
            "gdr_chunk_fwd", "gdr_chunk_bwd", "gdr_chunk_fwd_noalloc", "gdr_set_kernel_timers",
            "gdr_status_string", "gdr_last_error", "gdr_version")
+# include/gdr_rmsnorm.h: the fused RMSNorm backward and its reduction modes
+RMSNORM_EXPORTS = ("gdr_rmsnorm_bwd_workspace_bytes", "gdr_rmsnorm_bwd")
+GDR_REDUCE_FIXED, GDR_REDUCE_ATOMIC, GDR_REDUCE_SEPARATE = 0, 1, 2
 # size of the static workspace of gdr_chunk_fwd_noalloc (GDR_NOALLOC_SCRATCH_BYTES)
 GDR_NOALLOC_SCRATCH_BYTES = 64 << 20
 KERNELS = ("plan", "wy", "scan_fwd", "scan_bwd", "grad", "cp_scan_fwd", "cp_chain_fwd", "cp_scan_bwd",
@@ -89,6 +92,12 @@ def _open(path: str):
         lib.gdr_chunk_bwd.restype = ctypes.c_int
         lib.gdr_chunk_fwd_noalloc.argtypes = [P, vp, vp, vp, fp, fp, ip, fp, vp, fp, vp, vp]
         lib.gdr_chunk_fwd_noalloc.restype = ctypes.c_int
+        ci = ctypes.c_int
+        lib.gdr_rmsnorm_bwd_workspace_bytes.argtypes = [ci, ci, ci]
+        lib.gdr_rmsnorm_bwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.gdr_rmsnorm_bwd.argtypes = [ci, ci, ci, vp, fp, vp, fp, ctypes.c_float, vp, fp, ci, vp,
+                                        ctypes.c_size_t, vp]
+        lib.gdr_rmsnorm_bwd.restype = ctypes.c_int
         lib.gdr_set_kernel_timers.argtypes = [ctypes.c_void_p]
         lib.gdr_set_kernel_timers.restype = ctypes.c_int
         lib.gdr_status_string.argtypes = [ctypes.c_int]
@@ -180,6 +189,19 @@ def gdr_chunk_fwd_noalloc(p, q, k, v, beta, g, cu_seqlens, h0, o, hT, h_saved, s
     workspace); all tensor arguments are integer device addresses (0 = NULL)."""
     st = _h().gdr_chunk_fwd_noalloc(ctypes.byref(p), q, k, v, beta, g, cu_seqlens or None, h0 or None, o,
                                       hT or None, h_saved or None, stream or None)
+    return _raise_on(st) if check else st
+
+
+def gdr_rmsnorm_bwd_workspace_bytes(M: int, N: int, mode: int) -> int:
+    return _h().gdr_rmsnorm_bwd_workspace_bytes(int(M), int(N), int(mode))
+
+
+def gdr_rmsnorm_bwd(M, N, io_dtype, x, w, dy, rstd, eps, dx, dw, mode, ws, ws_bytes, stream,
+                    check=True) -> int:
+    """Raw call (include/gdr_rmsnorm.h); tensor arguments are integer device
+    addresses (0 = NULL)."""
+    st = _h().gdr_rmsnorm_bwd(int(M), int(N), int(io_dtype), x, w, dy, rstd or None, float(eps), dx, dw,
+                              int(mode), ws or None, ws_bytes, stream or None)
     return _raise_on(st) if check else st
 
 

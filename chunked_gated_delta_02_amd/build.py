@@ -32,7 +32,7 @@ PROBE_SOURCES = ["gdr_probe.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["gdr_fwd.hip", "gdr_bwd.hip", "gdr_api.cpp", "gdr_noalloc.hip"]
+SOURCES = ["gdr_fwd.hip", "gdr_bwd.hip", "gdr_api.cpp", "gdr_noalloc.hip", "gdr_rmsnorm.hip"]
 FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU instructions are kept off for all device code

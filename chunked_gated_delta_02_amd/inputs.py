@@ -118,3 +118,18 @@ def generate(w: Workload, device="cpu") -> dict:
             if out[key] is not None:
                 out[key] = out[key].to(device)
     return out
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm backward inputs (the M x N bf16 sweep of the quack PR #101 page,
+# "Rmsnorm backward fusing sum": M from 4k to 65k rows, N from 256 to 8k):
+# x ~ N(0, 1) and dy ~ N(0, 1) in the io dtype, w = 1 + 0.1 N(0, 1) fp32,
+# drawn in that order from torch.Generator('cpu').manual_seed(seed).
+
+def generate_rmsnorm(M: int, N: int, io_dtype: str = "bf16", seed: int = 0) -> dict:
+    gen = torch.Generator("cpu").manual_seed(seed)
+    x = torch.randn(M, N, generator=gen)
+    w = 1.0 + 0.1 * torch.randn(N, generator=gen)
+    dy = torch.randn(M, N, generator=gen)
+    dt = _DT[io_dtype]
+    return dict(x=x.to(dt), w=w.float(), dy=dy.to(dt))

@@ -204,3 +204,58 @@ def test_status_strings_and_version(lib):
     assert _lib.status_string(_lib.GDR_OK) == "GDR_OK"
     assert _lib.status_string(_lib.GDR_ERR_WORKSPACE) == "GDR_ERR_WORKSPACE"
     assert _lib.gdr_version() >= 100
+
+
+# ---------------------------------------------------------------------------
+# the fused RMSNorm backward (include/gdr_rmsnorm.h): exports and host checks
+
+def test_rmsnorm_header_functions_are_exported(lib):
+    text = open(os.path.join(ROOT, "include", "gdr_rmsnorm.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"\b(gdr_[a-z_0-9]+)\s*\(", text)))
+    assert set(names) == set(_lib.RMSNORM_EXPORTS), names
+    for n in names:
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value, n
+
+
+def _rn(M=64, N=256, io=None, mode=None, ws=FAKE, ws_bytes=None, **kw):
+    io = _lib.GDR_BF16 if io is None else io
+    mode = _lib.GDR_REDUCE_FIXED if mode is None else mode
+    a = dict(x=FAKE, w=FAKE, dy=FAKE, rstd=0, eps=1e-6, dx=FAKE, dw=FAKE)
+    a.update(kw)
+    if ws_bytes is None:
+        ws_bytes = _lib.gdr_rmsnorm_bwd_workspace_bytes(M, N, mode)
+    return _lib.gdr_rmsnorm_bwd(M, N, io, a["x"], a["w"], a["dy"], a["rstd"], a["eps"], a["dx"], a["dw"],
+                                mode, ws, ws_bytes, 0, check=False)
+
+
+def test_rmsnorm_workspace_sizes(lib):
+    # fixed: 512 B of counters + G partials + ceil(G/32) group sums (fp32);
+    # separate: counters + partials; atomic: none.  G = ceil(M/16), <= 1024
+    f = _lib.gdr_rmsnorm_bwd_workspace_bytes
+    assert f(64, 256, _lib.GDR_REDUCE_ATOMIC) == 0
+    assert f(64, 256, _lib.GDR_REDUCE_SEPARATE) == 512 + 4 * 256 * 4
+    assert f(64, 256, _lib.GDR_REDUCE_FIXED) == 512 + 4 * 256 * 4 + 1 * 256 * 4
+    assert f(65536, 8192, _lib.GDR_REDUCE_FIXED) == 512 + 1024 * 8192 * 4 + 32 * 8192 * 4
+    assert f(64, 12, _lib.GDR_REDUCE_FIXED) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=12), _lib.GDR_ERR_UNSUPPORTED),            # not a multiple of 8
+    (dict(N=8200), _lib.GDR_ERR_UNSUPPORTED),          # wider than 8192
+    (dict(M=-1), _lib.GDR_ERR_UNSUPPORTED),
+    (dict(io=_lib.GDR_F16), _lib.GDR_ERR_UNSUPPORTED),
+    (dict(mode=3), _lib.GDR_ERR_INVALID_ARG),
+    (dict(eps=-1.0), _lib.GDR_ERR_INVALID_ARG),        # rstd not given: eps must be >= 0
+    (dict(dx=0), _lib.GDR_ERR_INVALID_ARG),
+    (dict(w=FAKE + 4), _lib.GDR_ERR_INVALID_ARG),      # misaligned
+    (dict(ws=0), _lib.GDR_ERR_WORKSPACE),
+    (dict(ws_bytes=100), _lib.GDR_ERR_WORKSPACE),
+])
+def test_rmsnorm_invalid_arguments_return_before_any_launch(lib, kw, status):
+    assert _rn(**kw) == status
+    assert _lib.last_error() != ""
+
+
+def test_rmsnorm_no_rows_and_atomic_mode_need_nothing(lib):
+    assert _rn(M=0, x=0, w=0, dy=0, dx=0, dw=0, ws=0, ws_bytes=0) == _lib.GDR_OK
