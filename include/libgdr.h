@@ -97,7 +97,9 @@ typedef struct {
  * rounding; the forward and the backward of one problem may use different
  * cp_segments (the saved snapshots do not depend on it). */
 
-/* Validate a problem description.  Reads no tensor contents. */
+/* Validate a problem description.  Reads no tensor contents (the convention
+ * the support check of FastVideo PR #1819 follows, section "Semantics"):
+ * every decision is taken from the sizes, dtypes and flags alone. */
 gdr_status gdr_check(const gdr_problem* p);
 
 /* Workspace sizes in bytes (0 if the problem is invalid).  The backward
