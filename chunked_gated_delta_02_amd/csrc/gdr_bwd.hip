@@ -293,12 +293,16 @@ __global__ __launch_bounds__(256) void k_scan_bwd(const ScanBwdArgs a) {
 // ---------------------------------------------------------------------------
 // k_grad: per (chunk, head).  Phase 1 loops over DV in blocks of DVB and
 // accumulates the DV-contracted products (dQg, dKt, dW, dP, dT_V) in
-// registers while emitting dv; phase 2 finishes dq, dk, dbeta and dg.  Wave
-// Any of dq, dk, dv, dbeta, dg may be null: its stores are then dropped
-// (empty buffer range) or skipped; the computation is the same.  Wave
-// w owns output rows 16w..16w+15 of every 64-row product, so all row sums
-// stay inside one wavefront; column sums go through per-wave LDS partials
-// reduced in a fixed order.
+// registers while emitting dv; phase 2 finishes dq, dk, dbeta and dg.  Any
+// of dq, dk, dv, dbeta, dg may be null: its stores are then dropped (empty
+// buffer range) or skipped; the computation is the same.  Wave w owns output
+// rows 16w..16w+15 of every 64-row product, so all row sums stay inside one
+// wavefront; column sums go through per-wave LDS partials reduced in a fixed
+// order.  dVb (which becomes dv) is accumulated transposed (operands
+// swapped, see tr_row): each lane holds four consecutive columns of one row,
+// so a dv tile leaves in one 8-byte store per lane instead of four 2-byte
+// ones and beta is one factor per lane.  (dq and dk taken the same way
+// measured slower: the longer-lived row-major operands they need spill.)
 template <typename T, typename HS, int DK>
 __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const GradArgs a) {
   constexpr bool SPLIT = sizeof(T) == 2;
@@ -381,11 +385,14 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
     }
   }
   const int rw = 16 * w;            // first output row of this wave
-  const int r0 = rw + acc_row0();   // lane's rows r0..r0+3
+  const int r0 = rw + acc_row0();   // lane's rows r0..r0+3 (accumulator tiles)
+  const int rs = rw + tr_row();     // lane's row in transposed tiles
+  const int tc0 = tr_col0();        // and its first column there
 
   // per-lane row partials for the lane's 4 rows
   float rg[4] = {0.f, 0.f, 0.f, 0.f};   // dgamma row terms
   float rb[4] = {0.f, 0.f, 0.f, 0.f};   // dbeta row terms
+  float rbS = 0.f;                      // dbeta terms of row rs (transposed tiles)
   float gLh = 0.f;                      // <dh, h> partial (times e^{gamma_L} later)
   float gLy = 0.f;                      // sum of E rowsum(K * Delta dh^T) partial
 
@@ -512,7 +519,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
         if constexpr (SPLIT) aP[nt] = Mma<T>::mma(dof[ks], frag_colk_lds(sDeltaTl, L64, 16 * nt, ks * KW), aP[nt]);
       }
     }
-    // dVb = T^T dDelta (rows s = 16w): dv = beta dVb, dbeta += rowsum(V dVb)
+    // dVb = T^T dDelta, transposed tiles (lane: row s = rs, 4 columns):
+    // dv = beta dVb, dbeta += rowsum(V dVb)
     {
       f32x4 aVb[NTB];
 #pragma unroll
@@ -521,23 +529,16 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
       for (int ks = 0; ks < 64; ks += KW) {
         const frag at = frag_colk_lds(sT, L64, rw, ks);
 #pragma unroll
-        for (int nt = 0; nt < NTB; ++nt) aVb[nt] = Mma<T>::mma(at, frag_rowk(sDDt, L64, 16 * nt, ks), aVb[nt]);
+        for (int nt = 0; nt < NTB; ++nt) aVb[nt] = Mma<T>::mma(frag_rowk(sDDt, L64, 16 * nt, ks), at, aVb[nt]);
       }
       const __amdgpu_buffer_rsrc_t rdv = buf_rsrc((T*)a.dv + rowq * DV + dvb, a.dv ? len * H * DV * (int)sizeof(T) : 0);
-      const AccRows arv = acc_rows(H * DV, rw, (int)sizeof(T));
+      const float bs = sb[rs];
 #pragma unroll
       for (int nt = 0; nt < NTB; ++nt) {
-        f32x4 y;
+        const f32x4 vv = load4f(sV + rs * LDV + 16 * nt + tc0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int s = r0 + i;
-          const float x = aVb[nt][i];
-          y[i] = sb[s] * x;
-        }
-        const auto vv = lds_acc(sV, LDV, rw, 16 * nt);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) rb[i] += vv[i] * aVb[nt][i];
-        buf_store_acc<T>(rdv, arv, 16 * nt, y);
+        for (int i = 0; i < 4; ++i) rbS += vv[i] * aVb[nt][i];
+        buf_store4<T>(rdv, bs * aVb[nt], (rs * H * DV + tc0) * (int)sizeof(T), 16 * nt * (int)sizeof(T));
       }
     }
   }
@@ -779,15 +780,19 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
 #pragma unroll
     for (int nt = 0; nt < NTK; ++nt) buf_store_acc<T>(rdk, ark, 16 * nt, aKt[nt]);
   }
-  // row sums -> LDS (one writer per row), then dbeta, dgamma -> dg
+  // row sums -> LDS (one writer per row), then dbeta, dgamma -> dg.  The
+  // accumulator-tile terms of a row are spread over the 16 lanes sharing
+  // l >> 4, the transposed-tile terms over the 4 lanes sharing l & 15.
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     rg[i] = sum16(rg[i]);
     rb[i] = sum16(rb[i]);
   }
+  rbS = sum4g(rbS);
   GDR_SYNC();
   float* sRG = (float*)sQ;        // phase-2 LDS is free now
   float* sRB = sRG + 64;
+  float* sRB2 = sRB + 64;
   if ((l & 15) == 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -795,10 +800,14 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
       sRB[r0 + i] = rb[i];
     }
   }
+  if (l < 16) {
+    sRB2[rs] = rbS;
+  }
   GDR_SYNC();
   if (w == 0) {
-    float dgam = sRG[l] - (sRed[0 * 256 + 0 * 64 + l] + sRed[0 * 256 + 1 * 64 + l] + sRed[0 * 256 + 2 * 64 + l] +
-                           sRed[0 * 256 + 3 * 64 + l]) -
+    float dgam = sRG[l] -
+                 (sRed[0 * 256 + 0 * 64 + l] + sRed[0 * 256 + 1 * 64 + l] + sRed[0 * 256 + 2 * 64 + l] +
+                  sRed[0 * 256 + 3 * 64 + l]) -
                  (sRed[1 * 256 + 0 * 64 + l] + sRed[1 * 256 + 1 * 64 + l] + sRed[1 * 256 + 2 * 64 + l] +
                   sRed[1 * 256 + 3 * 64 + l]);
     if (l == 63) {
@@ -809,7 +818,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
     const float dgv = wave_suffix_scan(dgam);
     if (l < len) {
       if (a.dg) a.dg[(int64_t)(t0 + l) * H + h] = dgv;
-      if (a.dbeta) a.dbeta[(int64_t)(t0 + l) * H + h] = sRB[l];
+      if (a.dbeta) a.dbeta[(int64_t)(t0 + l) * H + h] = sRB[l] + sRB2[l];
     }
   }
 }

@@ -224,6 +224,31 @@ __device__ __forceinline__ f32x4 load4f(const T* p) {
   }
 }
 
+// Transposed accumulator tiles.  With the operands of C = A B swapped,
+// Mma<T>::mma(b, a, c) accumulates (A B)^T: the A and B fragments use the
+// same map of lanes, so nothing moves.  Lane l then holds row tr_row() of
+// A B and its four consecutive columns tr_col0() .. + 3 (relative to the
+// tile): one 8- or 16-byte piece of a row, stored or scaled per row with no
+// cross-lane exchange.
+__device__ __forceinline__ int tr_row() { return lane_id() & 15; }
+__device__ __forceinline__ int tr_col0() { return 4 * (lane_id() >> 4); }
+
+// Four consecutive elements of type T at byte offset voff + soff of a buffer
+// (one 8-byte store for 16-bit T, 16 bytes for fp32).  As for buf_store1,
+// the row part of the offset must be in voff, which the range check sees.
+template <typename T>
+__device__ __forceinline__ void buf_store4(__amdgpu_buffer_rsrc_t r, f32x4 v, int voff, int soff) {
+  if constexpr (sizeof(T) == 2) {
+    typedef T t4 __attribute__((ext_vector_type(4)));
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const t4 w = {from_f32<T>(v[0]), from_f32<T>(v[1]), from_f32<T>(v[2]), from_f32<T>(v[3])};
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, w), r, voff, soff, 0);
+  } else {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, soff, 0);
+  }
+}
+
 // launchers (return the HIP error of the launch)
 hipError_t launch_plan(const int* cu, int N, int T_total, int nchunks, int* seq_chunk, int* chunk_seq,
                        hipStream_t st);

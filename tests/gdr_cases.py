@@ -23,22 +23,25 @@ TOL = {"f32": 1e-5, "bf16": 5e-3}
 # row of a state h_T / dh0, and 64 consecutive tokens of one head of dbeta /
 # dg (a chunk's worth: single elements of these scalar outputs are too noisy
 # to bound tightly).  The 0.1 rms floor keeps rows of near-zero reference
-# norm from dominating.  The limits are about 1.5x the largest value measured
-# over every parity workload of the GPU tests (full-size workloads 1-4
-# included) with the kernels as they stand; the bf16 rows are dominated by
-# the rounding of outputs and MFMA operands to 8 significant bits (output
-# rounding alone gives about 1.5e-2 of a row's RMS at 10^5 rows), the fp32
-# ones by accumulation order.
+# norm from dominating.  The limits are about twice the largest value
+# measured over every parity workload of the GPU tests (full-size workloads
+# 1-4 included) and the smoke case, with the kernels as they stand.  The
+# bf16 rows are dominated by the rounding of outputs and MFMA operands to 8
+# significant bits (output rounding alone gives about 1.5e-2 of a row's RMS
+# at 10^5 rows; the worst rows of millions reach 4-9e-2), the fp32 ones by
+# accumulation order.  So on the bf16 path an error confined to a few rows is
+# seen once it exceeds about a tenth of its row's RMS; smaller localized
+# defects are left to the bitwise GPU-vs-GPU tests.
 _F32_EMAX, _F32_ROW = 1e-5, 6e-5
 EMAX_TOL = {
     "f32": {n: _F32_EMAX for n in ("o", "hT", "dq", "dk", "dv", "dbeta", "dg", "dh0")},
-    "bf16": {"o": 6e-3, "hT": 1e-3, "dq": 7.5e-3, "dk": 6e-3, "dv": 9e-3, "dbeta": 6e-3, "dg": 8e-3,
-             "dh0": 1.5e-3},
+    "bf16": {"o": 8e-3, "hT": 1.5e-3, "dq": 1e-2, "dk": 8e-3, "dv": 1.2e-2, "dbeta": 1.3e-2, "dg": 1.1e-2,
+             "dh0": 2e-3},
 }
 ROW_TOL = {
     "f32": {n: _F32_ROW for n in ("o", "hT", "dq", "dk", "dv", "dbeta", "dg", "dh0")},
-    "bf16": {"o": 2.5e-2, "hT": 4e-3, "dq": 6.5e-2, "dk": 9e-2, "dv": 7e-2, "dbeta": 6.5e-2, "dg": 7.5e-2,
-             "dh0": 1e-2},
+    "bf16": {"o": 3.5e-2, "hT": 6e-3, "dq": 9e-2, "dk": 1.2e-1, "dv": 1e-1, "dbeta": 1.7e-1, "dg": 1e-1,
+             "dh0": 1.5e-2},
 }
 OUTS_FWD = ("o", "hT")
 OUTS_BWD = ("dq", "dk", "dv", "dbeta", "dg", "dh0")

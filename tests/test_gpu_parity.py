@@ -395,3 +395,35 @@ def test_heads_independent_bitwise_across_tile_widths():
         for name in full:
             if full[name] is not None:
                 assert np.count_nonzero(_pick(full, name, idx) != sub[name]) == 0, "%s %s" % (w.name, name)
+
+
+@pytest.mark.parametrize("T1", [128, 100])
+def test_two_call_state_hand_off(T1):
+    # Resume: the forward over [0, T1) and then over [T1, T) from h0 = the
+    # first call's h_T gives one pass's o and h_T; the backward of the second
+    # call (with the pass's dh_T) hands its dh0 to the first call as dh_T,
+    # and the gradients of both calls together are the one pass's.  A
+    # chunk-aligned split (T1 = 128) keeps every chunk boundary of the single
+    # pass; a ragged one (T1 = 100) moves them, so it is held to the oracle.
+    w = C[1].replace(name="handoff", B=2, T=333, H=3, has_h0=True)
+    say("[case] two-call hand-off at T1 = %d" % T1)
+    inp = gin.generate(w)
+    one = run_gpu(w, inp)
+
+    def part(lo, hi, h0, dhT):
+        d = {k: (v[:, lo:hi].contiguous() if k in ("q", "k", "v", "beta", "g", "do") else v)
+             for k, v in inp.items()}
+        d["h0"], d["dhT"] = h0, dhT
+        return run_gpu(w.replace(name="handoff_%d_%d" % (lo, hi), T=hi - lo), d)
+
+    first = part(0, T1, inp["h0"], None)      # forward of part 1 (its backward is redone below)
+    hT1 = torch.from_numpy(first["hT"]).float()
+    second = part(T1, w.T, hT1, inp["dhT"])
+    dh_mid = torch.from_numpy(second["dh0"]).float()
+    first = part(0, T1, inp["h0"], dh_mid)
+    got = {n: np.concatenate([first[n], second[n]], axis=1) for n in ("o", "dq", "dk", "dv", "dbeta", "dg")}
+    got["hT"], got["dh0"] = second["hT"], first["dh0"]
+    if T1 % 64 == 0:
+        for n in got:
+            assert rel(got[n], one[n]) <= 1e-6, n
+    compare(w, got, run_oracle(w, inp))
