@@ -38,7 +38,7 @@
 namespace {
 
 constexpr int RN_GROUP = 32;          // workgroups per first-level group
-constexpr int RN_MAX_WG = 1024;       // most workgroups (row partitions) per call
+constexpr int RN_MAX_WG = 512;        // most workgroups (row partitions) per call
 constexpr int RN_MIN_ROWS = 16;       // fewest rows per workgroup
 constexpr int RN_COUNTERS = 512;      // bytes of counters at the start of the workspace (1 + 32 used)
 static_assert((1 + RN_MAX_WG / RN_GROUP) * 4 <= RN_COUNTERS, "counters fit their region");
@@ -46,17 +46,20 @@ constexpr int RN_MAX_N = 8192;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// 8 consecutive elements of a row (16 bytes of bf16, 32 of fp32) as fp32
+// 8 consecutive elements of a row (16 bytes of bf16, 32 of fp32), held as
+// loaded (so a prefetched row costs its raw size in registers) and widened
+// to fp32 where used
 template <typename T> struct Vec8;
 template <> struct Vec8<__bf16> {
-  static __device__ __forceinline__ void load(const __bf16* p, float* o) {
-    typedef __bf16 b8 __attribute__((ext_vector_type(8)));
-    const b8 v = *reinterpret_cast<const b8*>(p);
+  typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+  b8 d;
+  __device__ __forceinline__ void load(const __bf16* p) { d = *reinterpret_cast<const b8*>(p); }
+  __device__ __forceinline__ void zero() {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = (float)v[i];
+    for (int i = 0; i < 8; ++i) d[i] = (__bf16)0.f;
   }
+  __device__ __forceinline__ float operator[](int i) const { return (float)d[i]; }
   static __device__ __forceinline__ void store(__bf16* p, const float* o) {
-    typedef __bf16 b8 __attribute__((ext_vector_type(8)));
     b8 v;
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = (__bf16)o[i];
@@ -64,14 +67,13 @@ template <> struct Vec8<__bf16> {
   }
 };
 template <> struct Vec8<float> {
-  static __device__ __forceinline__ void load(const float* p, float* o) {
-    const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      o[i] = a[i];
-      o[4 + i] = b[i];
-    }
+  f32x4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const f32x4*>(p);
+    b = *reinterpret_cast<const f32x4*>(p + 4);
   }
+  __device__ __forceinline__ void zero() { a = b = (f32x4){0.f, 0.f, 0.f, 0.f}; }
+  __device__ __forceinline__ float operator[](int i) const { return i < 4 ? a[i] : b[i - 4]; }
   static __device__ __forceinline__ void store(float* p, const float* o) {
     *reinterpret_cast<f32x4*>(p) = (f32x4){o[0], o[1], o[2], o[3]};
     *reinterpret_cast<f32x4*>(p + 4) = (f32x4){o[4], o[5], o[6], o[7]};
@@ -101,28 +103,60 @@ struct RnArgs {
   float* gpart;       // [ceil(G / RN_GROUP)][N]: group sums
 };
 
-// sum_{k < n} p[k * N .. + 3] in order k = 0, 1, ..., loads issued 8 rows
-// at a time so that their latencies overlap
-__device__ __forceinline__ f32x4 sum_rows_in_order(const float* p, int N, int n) {
-  f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < n; k0 += 8) {
-    f32x4 v[8];
+// For the NC column pieces c = c0 + j * cstride (j < NC, 4 columns each,
+// those >= N skipped): out[j] = sum_{k < n} p[k * N + c .. + 3], added in
+// order k = 0, 1, ....  Loads are issued RB rows at a time for all NC pieces
+// together, so NC * RB loads per thread are in flight (one workgroup reading
+// a few MB on its own is bound by what it keeps in flight).
+template <int NC, int RB = 8>
+__device__ __forceinline__ void sum_rows_in_order(const float* p, int N, int n, int c0, int cstride, f32x4* out) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      v[u] = k0 + u < n ? *reinterpret_cast<const f32x4*>(p + (long)(k0 + u) * N) : (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < NC; ++j) out[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < n; k0 += RB) {
+    f32x4 v[NC][RB];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (k0 + u < n) acc += v[u];
+    for (int j = 0; j < NC; ++j)
+#pragma unroll
+      for (int u = 0; u < RB; ++u) {
+        const int c = c0 + j * cstride;
+        v[j][u] = (k0 + u < n && c < N) ? *reinterpret_cast<const f32x4*>(p + (long)(k0 + u) * N + c)
+                                        : (f32x4){0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+    for (int u = 0; u < RB; ++u)
+#pragma unroll
+      for (int j = 0; j < NC; ++j)
+        if (k0 + u < n) out[j] += v[j][u];
   }
-  return acc;
 }
 
-template <typename T, int TPR, int EPT>
-__global__ __launch_bounds__(256) void k_rmsnorm_bwd(const RnArgs a) {
-  constexpr int RPI = 256 / TPR;   // rows in flight per workgroup
+// dst[c] (+)= ordered sum over n rows of p, for every column piece of the
+// workgroup (NT threads, 4 columns per thread and piece)
+template <int NT, bool ADD>
+__device__ __forceinline__ void reduce_rows(const float* p, int N, int n, float* dst) {
+  constexpr int NC = 2;   // 16 loads in flight per thread; more would raise the kernel's register count
+  for (int cb = 4 * (int)threadIdx.x; cb < N; cb += NC * 4 * NT) {
+    f32x4 acc[NC];
+    sum_rows_in_order<NC>(p, N, n, cb, 4 * NT, acc);
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      const int c = cb + j * 4 * NT;
+      if (c < N) {
+        f32x4* d = reinterpret_cast<f32x4*>(dst + c);
+        *d = ADD ? *d + acc[j] : acc[j];
+      }
+    }
+  }
+}
+
+template <typename T, int NT, int TPR, int EPT>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 && EPT <= 16 ? 4 : 2, 8))) void k_rmsnorm_bwd(const RnArgs a) {
+  static_assert(TPR == 64 || TPR == NT, "a row is one wave or the whole workgroup");
+  constexpr int NW = NT / 64;      // waves
+  constexpr int RPI = NT / TPR;    // rows in flight per workgroup
   constexpr int NV = EPT / 8;      // 8-element pieces per thread
-  __shared__ __align__(16) float s_part[RN_MAX_N];   // the workgroup's dw partial
-  __shared__ float s_red[2][4];
+  extern __shared__ __align__(16) float s_part[];   // [N]: the workgroup's dw partial
+  __shared__ float s_red[2][NW];
   __shared__ int s_last;
   const int tid = threadIdx.x, wv = tid >> 6;
   const int slot = tid / TPR, t = tid % TPR;
@@ -147,36 +181,52 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const RnArgs a) {
   int red = 0;   // reductions so far (selects the LDS buffer of a cross-wave sum)
   auto row_sum = [&](float s) {
     s = wave_sum(s);
-    if constexpr (TPR == 256) {
+    if constexpr (TPR == NT && NW > 1) {
       float* buf = s_red[red & 1];
       if ((tid & 63) == 0) buf[wv] = s;
       __syncthreads();
-      s = ((buf[0] + buf[1]) + buf[2]) + buf[3];
+      s = buf[0];
+#pragma unroll
+      for (int k = 1; k < NW; ++k) s += buf[k];
       ++red;
     }
     return s;
   };
 
-  // TPR = 256: every thread runs every row (uniform trip count, barriers
-  // inside); TPR = 64: each wave runs its own rows, no barriers inside
-  for (long row = rb + slot; row < re; row += RPI) {
-    float xv[EPT], dyv[EPT];
+  // One row ahead: the next row's x and dy (and rstd) are loaded while the
+  // current one is computed.  TPR = NT: every thread runs every row (uniform
+  // trip count, barriers inside); TPR = 64: each wave runs its own rows.
+  Vec8<T> xr[NV], dr[NV];
+  float rr = 0.f;
+  auto issue = [&](long row) {
     const long base = row * (long)N;
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
       const int c = (t + TPR * v) * 8;
       if (c < N) {
-        Vec8<T>::load(xp + base + c, xv + 8 * v);
-        Vec8<T>::load(dyp + base + c, dyv + 8 * v);
+        xr[v].load(xp + base + c);
+        dr[v].load(dyp + base + c);
       } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) xv[8 * v + i] = dyv[8 * v + i] = 0.f;
+        xr[v].zero();
+        dr[v].zero();
       }
     }
-    float r;
-    if (a.rstd) {
-      r = a.rstd[row];
-    } else {
+    if (a.rstd) rr = a.rstd[row];
+  };
+  long row = rb + slot;
+  if (row < re) issue(row);
+  for (; row < re; row += RPI) {
+    float xv[EPT], dyv[EPT];
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        xv[8 * v + i] = xr[v][i];
+        dyv[8 * v + i] = dr[v][i];
+      }
+    float r = rr;
+    if (row + RPI < re) issue(row + RPI);
+    if (!a.rstd) {
       float ss = 0.f;
 #pragma unroll
       for (int i = 0; i < EPT; ++i) ss += xv[i] * xv[i];
@@ -193,6 +243,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const RnArgs a) {
       dxv[i] = r * (wv8[i] * dyv[i] - xh * cm);
       dwp[i] += dyv[i] * xh;
     }
+    const long base = row * (long)N;
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
       const int c = (t + TPR * v) * 8;
@@ -200,9 +251,9 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const RnArgs a) {
     }
   }
 
-  // the workgroup's partial in LDS: TPR = 256 owns every column once; with
-  // TPR = 64 the four waves hold the same columns and add in wave order
-  if constexpr (TPR == 256) {
+  // the workgroup's partial in LDS: TPR = NT owns every column once; with
+  // TPR = 64 the waves hold the same columns and add in wave order
+  if constexpr (TPR == NT) {
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
       const int c = (t + TPR * v) * 8;
@@ -212,7 +263,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const RnArgs a) {
     }
     __syncthreads();
   } else {
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < NW; ++k) {
       if (wv == k) {
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
@@ -227,11 +278,11 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const RnArgs a) {
   }
 
   if (a.mode == GDR_REDUCE_ATOMIC) {
-    for (int c = tid; c < N; c += 256) unsafeAtomicAdd(a.dw + c, s_part[c]);
+    for (int c = tid; c < N; c += NT) unsafeAtomicAdd(a.dw + c, s_part[c]);
     return;
   }
   float* mine = a.part + (long)g * N;
-  for (int c = 4 * tid; c < N; c += 1024)
+  for (int c = 4 * tid; c < N; c += 4 * NT)
     *reinterpret_cast<f32x4*>(mine + c) = *reinterpret_cast<const f32x4*>(s_part + c);
   if (a.mode == GDR_REDUCE_SEPARATE) return;
 
@@ -251,8 +302,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const RnArgs a) {
   if (!s_last) return;
   __threadfence();
   const int NG = (a.G + RN_GROUP - 1) / RN_GROUP;
-  for (int c = 4 * tid; c < N; c += 1024)
-    *reinterpret_cast<f32x4*>(a.gpart + (long)grp * N + c) = sum_rows_in_order(a.part + (long)g0 * N + c, N, members);
+  reduce_rows<NT, false>(a.part + (long)g0 * N, N, members, a.gpart + (long)grp * N);
   __syncthreads();
   if (tid == 0) {
     __hip_atomic_store(a.cnt + 1 + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -262,25 +312,34 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const RnArgs a) {
   __syncthreads();
   if (!s_last) return;
   __threadfence();
-  for (int c = 4 * tid; c < N; c += 1024) {
-    f32x4* d = reinterpret_cast<f32x4*>(a.dw + c);
-    *d = *d + sum_rows_in_order(a.gpart + c, N, NG);
-  }
+  reduce_rows<NT, true>(a.gpart, N, NG, a.dw);
   if (tid == 0) __hip_atomic_store(a.cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // separate mode, second kernel: dw[c] += sum over workgroups (in order);
-// one thread per 4 columns
-__global__ __launch_bounds__(256) void k_rmsnorm_reduce(const float* part, int G, int N, float* dw) {
-  const int c = 4 * (blockIdx.x * 256 + threadIdx.x);
-  if (c >= N) return;
-  f32x4* d = reinterpret_cast<f32x4*>(dw + c);
-  *d = *d + sum_rows_in_order(part + c, N, G);
+// 4 columns per thread and piece, RN_RED_COLS columns per workgroup
+constexpr int RN_RED_COLS = 256;
+__global__ __launch_bounds__(64) void k_rmsnorm_reduce(const float* part, int G, int N, float* dw) {
+  const int c = blockIdx.x * RN_RED_COLS + 4 * (int)threadIdx.x;
+  f32x4 acc;
+  sum_rows_in_order<1, 16>(part, N, G, c, 0, &acc);
+  if (c < N) {
+    f32x4* d = reinterpret_cast<f32x4*>(dw + c);
+    *d = *d + acc;
+  }
 }
 
-int workgroups(long M) {
+// Workgroups (row partitions): at least RN_MIN_ROWS rows each, and at most
+// one per compute unit (256 on MI355X) -- or two where a row of N <= 2048 is
+// spread over the whole workgroup, whose barrier per row a second workgroup
+// on the CU hides.  Fewer partials shorten the fixed-order reduction at the
+// end, and one workgroup per CU already keeps enough rows in flight (with
+// the one-row prefetch) for the rest; measured over the sweep against caps
+// of 384, 512 and 1024.
+int workgroups(long M, int N) {
+  const long cap = (N > 1024 && N <= 2048) ? 512 : 256;
   const long g = (M + RN_MIN_ROWS - 1) / RN_MIN_ROWS;
-  return (int)(g < 1 ? 1 : (g > RN_MAX_WG ? RN_MAX_WG : g));
+  return (int)(g < 1 ? 1 : (g > cap ? cap : g));
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -292,7 +351,7 @@ struct Layout {
 Layout layout(long M, int N, int mode) {
   Layout l;
   if (mode == GDR_REDUCE_ATOMIC) return l;
-  const int G = workgroups(M), NG = (G + RN_GROUP - 1) / RN_GROUP;
+  const int G = workgroups(M, N), NG = (G + RN_GROUP - 1) / RN_GROUP;
   l.part = RN_COUNTERS;
   l.gpart = align256(l.part + (size_t)G * N * 4);
   l.total = mode == GDR_REDUCE_FIXED ? align256(l.gpart + (size_t)NG * N * 4) : align256(l.gpart);
@@ -301,19 +360,19 @@ Layout layout(long M, int N, int mode) {
 
 bool bad_align(const void* p) { return ((uintptr_t)p & 15) != 0; }
 
-template <typename T, int TPR, int EPT>
+template <typename T, int NT, int TPR, int EPT>
 hipError_t launch(const RnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((k_rmsnorm_bwd<T, TPR, EPT>), dim3(a.G), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((k_rmsnorm_bwd<T, NT, TPR, EPT>), dim3(a.G), dim3(NT), (size_t)a.N * sizeof(float), s, a);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_t(const RnArgs& a, hipStream_t s) {
-  if (a.N <= 512) return launch<T, 64, 8>(a, s);
-  if (a.N <= 1024) return launch<T, 64, 16>(a, s);
-  if (a.N <= 2048) return launch<T, 64, 32>(a, s);
-  if (a.N <= 4096) return launch<T, 256, 16>(a, s);
-  return launch<T, 256, 32>(a, s);
+  if (a.N <= 512) return launch<T, 256, 64, 8>(a, s);
+  if (a.N <= 1024) return launch<T, 256, 64, 16>(a, s);
+  if (a.N <= 2048) return launch<T, 256, 256, 8>(a, s);
+  if (a.N <= 4096) return launch<T, 256, 256, 16>(a, s);
+  return launch<T, 256, 256, 32>(a, s);
 }
 
 }  // namespace
@@ -373,7 +432,7 @@ gdr_status gdr_rmsnorm_bwd(int M, int N, int io_dtype, const void* x, const floa
     }
   }
   RnArgs a{};
-  a.M = M; a.N = N; a.G = workgroups(M); a.mode = mode; a.eps = eps;
+  a.M = M; a.N = N; a.G = workgroups(M, N); a.mode = mode; a.eps = eps;
   a.x = x; a.w = w; a.dy = dy; a.rstd = rstd; a.dx = dx; a.dw = dw;
   a.cnt = ws ? (unsigned*)ws : nullptr;
   a.part = ws ? (float*)(ws + l.part) : nullptr;
@@ -381,7 +440,7 @@ gdr_status gdr_rmsnorm_bwd(int M, int N, int io_dtype, const void* x, const floa
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = io_dtype == GDR_BF16 ? launch_t<__bf16>(a, s) : launch_t<float>(a, s);
   if (e == hipSuccess && mode == GDR_REDUCE_SEPARATE) {
-    hipLaunchKernelGGL(k_rmsnorm_reduce, dim3((N / 4 + 255) / 256), dim3(256), 0, s, (const float*)a.part, a.G, N, dw);
+    hipLaunchKernelGGL(k_rmsnorm_reduce, dim3((N + RN_RED_COLS - 1) / RN_RED_COLS), dim3(64), 0, s, (const float*)a.part, a.G, N, dw);
     e = hipGetLastError();
   }
   if (e != hipSuccess) {

@@ -231,12 +231,14 @@ def _rn(M=64, N=256, io=None, mode=None, ws=FAKE, ws_bytes=None, **kw):
 
 def test_rmsnorm_workspace_sizes(lib):
     # fixed: 512 B of counters + G partials + ceil(G/32) group sums (fp32);
-    # separate: counters + partials; atomic: none.  G = ceil(M/16), <= 1024
+    # separate: counters + partials; atomic: none.  G = ceil(M/16), at most
+    # 256 (512 for 1024 < N <= 2048)
     f = _lib.gdr_rmsnorm_bwd_workspace_bytes
     assert f(64, 256, _lib.GDR_REDUCE_ATOMIC) == 0
     assert f(64, 256, _lib.GDR_REDUCE_SEPARATE) == 512 + 4 * 256 * 4
     assert f(64, 256, _lib.GDR_REDUCE_FIXED) == 512 + 4 * 256 * 4 + 1 * 256 * 4
-    assert f(65536, 8192, _lib.GDR_REDUCE_FIXED) == 512 + 1024 * 8192 * 4 + 32 * 8192 * 4
+    assert f(65536, 8192, _lib.GDR_REDUCE_FIXED) == 512 + 256 * 8192 * 4 + 8 * 8192 * 4
+    assert f(65536, 2048, _lib.GDR_REDUCE_FIXED) == 512 + 512 * 2048 * 4 + 16 * 2048 * 4
     assert f(64, 12, _lib.GDR_REDUCE_FIXED) == 0
 
 

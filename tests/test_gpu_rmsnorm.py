@@ -77,7 +77,7 @@ def test_dw_is_accumulated_into():
 
 
 def test_fixed_and_separate_modes_are_bitwise_reproducible_and_counters_return_to_zero():
-    M, N = 20000, 2048    # 1024 workgroups: 32 first-level groups
+    M, N = 20000, 2048    # 512 workgroups: 16 first-level groups
     for mode in ("fixed", "separate"):
         ws = rmsnorm.workspace(M, N, mode, torch.device("cuda:0"))
         first = None
