@@ -8,7 +8,9 @@ backward) as hand-written gfx950 HIP kernels behind a C ABI
 The HIP library is loaded on first use; if it has not been built the call
 raises (there is no CPU or PyTorch fallback).
 """
-from .ops import ChunkGDRFunction, chunk_gdr, chunk_gdr_bwd, chunk_gdr_fwd, make_problem  # noqa: F401
+from .ops import (ChunkGDRFunction, chunk_gdr, chunk_gdr_bwd, chunk_gdr_fwd, make_problem,  # noqa: F401
+                  validate_cu_seqlens)
 from ._lib import GDRError  # noqa: F401
 
-__all__ = ["chunk_gdr", "chunk_gdr_fwd", "chunk_gdr_bwd", "ChunkGDRFunction", "make_problem", "GDRError"]
+__all__ = ["chunk_gdr", "chunk_gdr_fwd", "chunk_gdr_bwd", "ChunkGDRFunction", "make_problem", "GDRError",
+           "validate_cu_seqlens"]

@@ -22,8 +22,8 @@ GDR_LAYOUT_KV, GDR_LAYOUT_VK = 0, 1
 
 # every function the header declares, for the export check
 EXPORTS = ("gdr_check", "gdr_fwd_workspace_bytes", "gdr_bwd_workspace_bytes", "gdr_h_saved_bytes",
-           "gdr_chunk_fwd", "gdr_chunk_bwd", "gdr_chunk_fwd_noalloc", "gdr_set_kernel_timers",
-           "gdr_status_string", "gdr_last_error", "gdr_version")
+           "gdr_chunk_fwd", "gdr_chunk_bwd", "gdr_chunk_fwd_noalloc", "gdr_validate_cu_seqlens",
+           "gdr_set_kernel_timers", "gdr_status_string", "gdr_last_error", "gdr_version")
 # include/gdr_rmsnorm.h: the fused RMSNorm backward and its reduction modes
 RMSNORM_EXPORTS = ("gdr_rmsnorm_bwd_workspace_bytes", "gdr_rmsnorm_bwd")
 GDR_REDUCE_FIXED, GDR_REDUCE_ATOMIC, GDR_REDUCE_SEPARATE = 0, 1, 2
@@ -93,6 +93,8 @@ def _open(path: str):
         lib.gdr_chunk_fwd_noalloc.argtypes = [P, vp, vp, vp, fp, fp, ip, fp, vp, fp, vp, vp]
         lib.gdr_chunk_fwd_noalloc.restype = ctypes.c_int
         ci = ctypes.c_int
+        lib.gdr_validate_cu_seqlens.argtypes = [ip, ci, ci, ip, vp]
+        lib.gdr_validate_cu_seqlens.restype = ci
         lib.gdr_rmsnorm_bwd_workspace_bytes.argtypes = [ci, ci, ci]
         lib.gdr_rmsnorm_bwd_workspace_bytes.restype = ctypes.c_size_t
         lib.gdr_rmsnorm_bwd.argtypes = [ci, ci, ci, vp, fp, vp, fp, ctypes.c_float, vp, fp, ci, vp,
@@ -189,6 +191,15 @@ def gdr_chunk_fwd_noalloc(p, q, k, v, beta, g, cu_seqlens, h0, o, hT, h_saved, s
     workspace); all tensor arguments are integer device addresses (0 = NULL)."""
     st = _h().gdr_chunk_fwd_noalloc(ctypes.byref(p), q, k, v, beta, g, cu_seqlens or None, h0 or None, o,
                                       hT or None, h_saved or None, stream or None)
+    return _raise_on(st) if check else st
+
+
+def gdr_validate_cu_seqlens(cu_seqlens, num_seqs, total_tokens, result, stream, check=True) -> int:
+    """Raw call: launches the device check of a packed batch's cu_seqlens;
+    the kernel writes the first violating index (or -1) to the device int at
+    `result`.  Addresses are integers (0 = NULL)."""
+    st = _h().gdr_validate_cu_seqlens(cu_seqlens or None, int(num_seqs), int(total_tokens), result or None,
+                                      stream or None)
     return _raise_on(st) if check else st
 
 

@@ -376,6 +376,24 @@ const char* gdr_status_string(gdr_status s) {
 
 const char* gdr_last_error(void) { return g_err; }
 
+gdr_status gdr_validate_cu_seqlens(const int32_t* cu_seqlens, int num_seqs, int total_tokens, int32_t* result,
+                                   void* stream) {
+  g_err[0] = 0;
+  if (!cu_seqlens || !result) { set_err("cu_seqlens and result are required"); return GDR_ERR_INVALID_ARG; }
+  if (num_seqs < 1 || num_seqs > GDR_MAX_SEQS) {
+    set_err("num_seqs must be in [1, %d] (got %d)", GDR_MAX_SEQS, num_seqs);
+    return GDR_ERR_INVALID_ARG;
+  }
+  if (total_tokens < 0) { set_err("total_tokens must be >= 0 (got %d)", total_tokens); return GDR_ERR_INVALID_ARG; }
+  if (((uintptr_t)cu_seqlens & 3) || ((uintptr_t)result & 3)) {
+    set_err("cu_seqlens and result must be 4-byte aligned");
+    return GDR_ERR_INVALID_ARG;
+  }
+  const hipError_t e = gdr::launch_check_cu(cu_seqlens, num_seqs, total_tokens, result, (hipStream_t)stream);
+  if (e != hipSuccess) { set_err("launch failed: %s", hipGetErrorString(e)); return GDR_ERR_HIP; }
+  return GDR_OK;
+}
+
 gdr_status gdr_set_kernel_timers(void* const* events) {
   g_err[0] = 0;
   if (!events) {

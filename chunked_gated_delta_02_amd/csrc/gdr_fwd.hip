@@ -22,6 +22,8 @@
 //   k_scan_fwd  serial over chunks per (sequence, head, DV tile): the state
 //               tile lives in registers (fp32 MFMA accumulators) with a bf16
 //               copy in LDS; writes per-chunk snapshots, o and h_T
+#include <climits>
+
 #include "gdr_kernels.h"
 
 namespace gdr {
@@ -802,6 +804,35 @@ static hipError_t launch_wy_t(const WyArgs& a, hipStream_t st) {
 hipError_t launch_plan(const int* cu, int N, int T_total, int nchunks, int* seq_chunk, int* chunk_seq,
                        hipStream_t st) {
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, cu, N, T_total, nchunks, seq_chunk, chunk_seq);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// k_check_cu: one workgroup of 1024 threads checks the packed-batch contract
+// of cu_seqlens (cu[0] = 0, every later entry in [previous entry, T_total])
+// and writes to *result the smallest index of an entry that breaks it, or -1.
+// The kernel writes its result unconditionally, so the buffer needs no
+// clearing beforehand.
+__global__ __launch_bounds__(1024) void k_check_cu(const int* cu, int N, int T_total, int* result) {
+  __shared__ int s_min[1024];
+  const int tid = threadIdx.x;
+  int bad = INT_MAX;
+  for (int i = tid; i <= N; i += 1024) {
+    const int c = cu[i];
+    const bool ok = i == 0 ? c == 0 : (c >= cu[i - 1] && c <= T_total);
+    if (!ok) bad = min(bad, i);
+  }
+  s_min[tid] = bad;
+  GDR_SYNC();
+  for (int d = 512; d > 0; d >>= 1) {
+    if (tid < d) s_min[tid] = min(s_min[tid], s_min[tid + d]);
+    GDR_SYNC();
+  }
+  if (tid == 0) *result = s_min[0] == INT_MAX ? -1 : s_min[0];
+}
+
+hipError_t launch_check_cu(const int* cu, int N, int T_total, int* result, hipStream_t st) {
+  hipLaunchKernelGGL(k_check_cu, dim3(1), dim3(1024), 0, st, cu, N, T_total, result);
   return hipGetLastError();
 }
 

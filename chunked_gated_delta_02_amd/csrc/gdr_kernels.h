@@ -252,6 +252,7 @@ __device__ __forceinline__ void buf_store4(__amdgpu_buffer_rsrc_t r, f32x4 v, in
 // launchers (return the HIP error of the launch)
 hipError_t launch_plan(const int* cu, int N, int T_total, int nchunks, int* seq_chunk, int* chunk_seq,
                        hipStream_t st);
+hipError_t launch_check_cu(const int* cu, int N, int T_total, int* result, hipStream_t st);
 hipError_t launch_wy(const WyArgs& a, bool f32, int DK, bool bwd, hipStream_t st);
 // mode 0: CP segment summaries; forward 1: snapshots only, 2: snapshots and
 // output; backward 1: the reverse scan proper

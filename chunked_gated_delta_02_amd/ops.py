@@ -13,6 +13,7 @@ is ``h_store="f16"``).
 """
 from __future__ import annotations
 
+import os
 from typing import Optional
 
 import torch
@@ -80,6 +81,33 @@ def _check_tensors(q, k, v, beta, g, cu_seqlens, extra=()):
             raise ValueError("cu_seqlens must be a contiguous int32 tensor on the same device")
 
 
+def validate_cu_seqlens(cu_seqlens: torch.Tensor, total_tokens: int) -> None:
+    """Check a packed batch's cu_seqlens on the device (``gdr_validate_cu_seqlens``:
+    cu[0] = 0, every later entry in [previous entry, total_tokens]) and raise
+    ValueError naming the first entry that breaks it.  Synchronises with the
+    current stream to read the result."""
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous() \
+            or cu_seqlens.device.type != "cuda":
+        raise ValueError("cu_seqlens must be a contiguous 1-D int32 tensor on a cuda device")
+    if cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens needs at least two entries")
+    res = torch.empty(1, dtype=torch.int32, device=cu_seqlens.device)
+    stream = torch.cuda.current_stream(cu_seqlens.device).cuda_stream
+    _lib.gdr_validate_cu_seqlens(cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, int(total_tokens),
+                                 res.data_ptr(), stream)
+    bad = int(res.item())
+    if bad >= 0:
+        raise ValueError("cu_seqlens[%d] breaks the packed-batch contract (cu[0] = 0, non-decreasing, "
+                         "cu[-1] <= %d)" % (bad, total_tokens))
+
+
+def _maybe_validate(cu_seqlens, total_tokens):
+    # GDR_VALIDATE=1: check every packed batch's cu_seqlens before the call
+    # (a synchronising debug aid; off by default)
+    if cu_seqlens is not None and os.environ.get("GDR_VALIDATE", "0") == "1":
+        validate_cu_seqlens(cu_seqlens, total_tokens)
+
+
 def _state_shape(N, H, DK, DV, layout):
     return (N, H, DK, DV) if layout == "KV" else (N, H, DV, DK)
 
@@ -97,6 +125,7 @@ def chunk_gdr_fwd(q, k, v, beta, g, cu_seqlens=None, h0=None, layout="KV", scale
     st = _lib.gdr_check(p)
     if st != _lib.GDR_OK:
         raise _lib.GDRError(st, _lib.last_error())
+    _maybe_validate(cu_seqlens, T)
     o = torch.empty(B, T, H, DV, dtype=q.dtype, device=q.device)
     hT = torch.empty(_state_shape(N, H, DK, DV, layout), dtype=torch.float32, device=q.device) \
         if output_final_state else None
@@ -134,6 +163,7 @@ def chunk_gdr_bwd(q, k, v, beta, g, do, cu_seqlens=None, h0=None, dhT=None, h_sa
         raise _lib.GDRError(st, _lib.last_error())
     if h_saved is not None and h_saved.numel() * h_saved.element_size() < _lib.gdr_h_saved_bytes(p):
         raise ValueError("h_saved is smaller than gdr_h_saved_bytes()")
+    _maybe_validate(cu_seqlens, T)
     unknown = set(need) - set(GRADS)
     if unknown:
         raise ValueError("unknown gradient names %s" % sorted(unknown))

@@ -151,6 +151,22 @@ gdr_status gdr_chunk_fwd_noalloc(const gdr_problem* p, const void* q, const void
                                  const float* beta, const float* g, const int32_t* cu_seqlens,
                                  const float* h0, void* o, float* hT, void* h_saved, void* stream);
 
+/* Checks, on the device, the contract of a packed batch's cu_seqlens that
+ * gdr_chunk_fwd / gdr_chunk_bwd assume without reading it on the host:
+ * cu_seqlens[0] = 0 and every later entry in [previous entry, total_tokens].
+ * One kernel is launched on `stream`; it writes to the device int *result
+ * the smallest index i in [0, num_seqs] whose entry breaks the contract, or
+ * -1 if none does (result needs no clearing beforehand; read it after the
+ * stream has passed the launch).  The forward and backward themselves clamp
+ * a broken cu_seqlens into range, so it cannot make them read or write out
+ * of bounds, but their results are then unspecified; this check (which the
+ * Python binding runs before each packed call when GDR_VALIDATE=1 is set in
+ * the environment) says so explicitly.  Arguments: num_seqs in [1, 8192],
+ * total_tokens >= 0, both pointers non-NULL and 4-byte aligned; otherwise an
+ * error is returned and nothing is launched. */
+gdr_status gdr_validate_cu_seqlens(const int32_t* cu_seqlens, int num_seqs, int total_tokens, int32_t* result,
+                                   void* stream);
+
 /* Diagnostics: per-kernel timing with caller-owned HIP events.
  * Kernel ids of the launches a forward / backward call makes: */
 enum {

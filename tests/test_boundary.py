@@ -261,3 +261,20 @@ def test_rmsnorm_invalid_arguments_return_before_any_launch(lib, kw, status):
 
 def test_rmsnorm_no_rows_and_atomic_mode_need_nothing(lib):
     assert _rn(M=0, x=0, w=0, dy=0, dx=0, dw=0, ws=0, ws_bytes=0) == _lib.GDR_OK
+
+
+# gdr_validate_cu_seqlens: every invalid argument returns before any launch
+@pytest.mark.parametrize("kw,status", [
+    (dict(cu=0), _lib.GDR_ERR_INVALID_ARG),
+    (dict(res=0), _lib.GDR_ERR_INVALID_ARG),
+    (dict(n=0), _lib.GDR_ERR_INVALID_ARG),
+    (dict(n=8193), _lib.GDR_ERR_INVALID_ARG),       # beyond the packed-batch maximum
+    (dict(t=-1), _lib.GDR_ERR_INVALID_ARG),
+    (dict(cu=FAKE + 2), _lib.GDR_ERR_INVALID_ARG),  # misaligned
+    (dict(res=FAKE + 1), _lib.GDR_ERR_INVALID_ARG),
+])
+def test_validate_cu_seqlens_invalid_arguments(lib, kw, status):
+    a = dict(cu=FAKE, n=4, t=100, res=FAKE)
+    a.update(kw)
+    assert _lib.gdr_validate_cu_seqlens(a["cu"], a["n"], a["t"], a["res"], 0, check=False) == status
+    assert _lib.last_error() != ""
