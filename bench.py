@@ -54,6 +54,8 @@ def parse():
                          "(outside the timed intervals; 0 = no flush)")
     ap.add_argument("--cp-segments", type=int, default=None,
                     help="intra-card context-parallel segments per sequence (default: the workload's)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step recorded into a HIP graph and replayed (ms_per_step_graph)")
     ap.add_argument("--recompute", action="store_true",
                     help="the forward keeps no state snapshots and the backward recomputes them "
                          "(default: the forward saves them for the backward)")
@@ -550,13 +552,13 @@ def main():
     stream = torch.cuda.current_stream(dev).cuda_stream
     P = lambda t: 0 if t is None else t.data_ptr()
 
-    def fwd():
+    def fwd(st=None):
         _lib.gdr_chunk_fwd(p, P(q), P(k), P(v), P(beta), P(g), P(cu), P(h0), P(o), P(hT), P(h_saved),
-                           P(wsf), fws, stream)
+                           P(wsf), fws, stream if st is None else st)
 
-    def bwd():
+    def bwd(st=None):
         _lib.gdr_chunk_bwd(p, P(q), P(k), P(v), P(beta), P(g), P(cu), P(h0), P(h_saved), P(do), P(dhT),
-                           P(dq), P(dk), P(dv), P(dbeta), P(dg), P(dh0), P(wsb), bws, stream)
+                           P(dq), P(dk), P(dv), P(dbeta), P(dg), P(dh0), P(wsb), bws, stream if st is None else st)
 
     hip = Hip()
     nk = len(_lib.KERNELS)
@@ -645,6 +647,31 @@ def main():
         for tup in evl:
             for e_ in tup:
                 hip.destroy(e_)
+    graph_ms = None
+    if args.graph:
+        # the same step recorded once into a HIP graph (the library issues
+        # only kernel launches) and replayed, flushed and timed like pass A
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            cs = torch.cuda.current_stream(dev).cuda_stream
+            fwd(cs)
+            bwd(cs)
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            gr.replay()
+        sevg = [(hip.event(), hip.event()) for _ in range(args.steps)]
+        for s in range(args.steps):
+            if flush is not None:
+                flush.fill_(float(s))
+            hip.record(sevg[s][0], stream)
+            gr.replay()
+            hip.record(sevg[s][1], stream)
+        torch.cuda.synchronize()
+        graph_ms = [hip.elapsed_ms(a, b) for a, b in sevg]
+        for tup in sevg:
+            for e_ in tup:
+                hip.destroy(e_)
+        del gr
     del flush
     peaks = None
     if not args.no_probe:
@@ -744,6 +771,10 @@ def main():
         "peaks_measured": peaks,
         "cpu_baseline": None,
     }
+    if graph_ms is not None:
+        res["ms_per_step_graph"] = round(med(graph_ms), 4)
+        res["graph_note"] = ("the same step recorded into one HIP graph and replayed; median of %d replays, "
+                             "flushed like pass A (value stays the eager pass)" % len(graph_ms))
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
     print(json.dumps(res), flush=True)
