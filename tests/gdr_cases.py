@@ -25,23 +25,28 @@ TOL = {"f32": 1e-5, "bf16": 5e-3}
 # to bound tightly).  The 0.1 rms floor keeps rows of near-zero reference
 # norm from dominating.  The limits are about twice the largest value
 # measured over every parity workload of the GPU tests (full-size workloads
-# 1-4 included) and the smoke case, with the kernels as they stand.  The
+# 1-4 included), the 24 drawn cases of test_gpu_random.py and the smoke
+# case, with the kernels as they stand.  The drawn cases set the larger
+# limits: rows of dh0 and 64-token blocks of dbeta / dg whose RMS is a few
+# times below the tensor's (strong decay with an initial state), and the
+# fp32 path's dg at the last token of a strongly decaying sequence.  The
 # bf16 rows are dominated by the rounding of outputs and MFMA operands to 8
 # significant bits (output rounding alone gives about 1.5e-2 of a row's RMS
 # at 10^5 rows; the worst rows of millions reach 4-9e-2), the fp32 ones by
 # accumulation order.  So on the bf16 path an error confined to a few rows is
 # seen once it exceeds about a tenth of its row's RMS; smaller localized
 # defects are left to the bitwise GPU-vs-GPU tests.
-_F32_EMAX, _F32_ROW = 1e-5, 6e-5
 EMAX_TOL = {
-    "f32": {n: _F32_EMAX for n in ("o", "hT", "dq", "dk", "dv", "dbeta", "dg", "dh0")},
-    "bf16": {"o": 8e-3, "hT": 1.5e-3, "dq": 1e-2, "dk": 8e-3, "dv": 1.2e-2, "dbeta": 1.3e-2, "dg": 1.1e-2,
+    "f32": {"o": 1e-5, "hT": 1e-5, "dq": 1e-5, "dk": 1e-5, "dv": 1.5e-5, "dbeta": 1.2e-5, "dg": 3e-5,
+            "dh0": 1e-5},
+    "bf16": {"o": 8e-3, "hT": 1.5e-3, "dq": 1e-2, "dk": 9e-3, "dv": 1.2e-2, "dbeta": 1.3e-2, "dg": 1.2e-2,
              "dh0": 2e-3},
 }
 ROW_TOL = {
-    "f32": {n: _F32_ROW for n in ("o", "hT", "dq", "dk", "dv", "dbeta", "dg", "dh0")},
-    "bf16": {"o": 3.5e-2, "hT": 6e-3, "dq": 9e-2, "dk": 1.2e-1, "dv": 1e-1, "dbeta": 1.7e-1, "dg": 1e-1,
-             "dh0": 1.5e-2},
+    "f32": {"o": 8e-5, "hT": 8e-5, "dq": 9e-5, "dk": 8e-5, "dv": 1e-4, "dbeta": 1.3e-4, "dg": 2e-4,
+            "dh0": 6e-5},
+    "bf16": {"o": 3.5e-2, "hT": 6e-3, "dq": 9.5e-2, "dk": 1.2e-1, "dv": 1e-1, "dbeta": 3e-1, "dg": 1.2e-1,
+             "dh0": 1.1e-1},
 }
 OUTS_FWD = ("o", "hT")
 OUTS_BWD = ("dq", "dk", "dv", "dbeta", "dg", "dh0")

