@@ -301,10 +301,15 @@ class Probe:
                           % (blocks, iters)}
 
 
+# the translation unit the counted kernel (k_grad) is compiled from
+GRAD_SOURCES = ("chunked_gated_delta_02_amd/csrc/gdr_bwd.hip", "chunked_gated_delta_02_amd/csrc/gdr_kernels.h",
+                "chunked_gated_delta_02_amd/csrc/gdr_device.h", "include/libgdr.h")
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.join(ROOT, "chunked_gated_delta_02_amd", "csrc"))):
-        with open(os.path.join(ROOT, "chunked_gated_delta_02_amd", "csrc", f), "rb") as fh:
+    for f in GRAD_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 

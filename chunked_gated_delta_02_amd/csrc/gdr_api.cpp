@@ -417,6 +417,7 @@ gdr_status gdr_debug_set_delay(int wave, int mod, int iters, int salt) {
   const gdr::DelayCfg c{wave, mod, iters, salt};
   GDR_TRY(gdr::debug_set_delay_fwd(c));
   GDR_TRY(gdr::debug_set_delay_bwd(c));
+  GDR_TRY(gdr::debug_set_delay_rmsnorm(c));
   return GDR_OK;
 }
 #endif

@@ -264,6 +264,7 @@ hipError_t launch_grad(const GradArgs& a, bool f32, int hs_dtype, int DK, hipStr
 // barrier-delay settings of the kernels in each source file (race-test build)
 hipError_t debug_set_delay_fwd(const DelayCfg& c);
 hipError_t debug_set_delay_bwd(const DelayCfg& c);
+hipError_t debug_set_delay_rmsnorm(const DelayCfg& c);
 #endif
 
 }  // namespace gdr

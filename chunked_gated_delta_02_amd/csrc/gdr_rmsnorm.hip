@@ -34,8 +34,27 @@
 
 #include "gdr_host.h"
 #include "gdr_rmsnorm.h"
+#ifdef GDR_DEBUG_DELAY
+#include "gdr_kernels.h"   // the race-test build's delay hook (gdr_device.h)
+#endif
 
 namespace {
+
+// Barriers, and the points around the cross-workgroup hand-offs of the
+// fixed-order reduction, where the race-test build (GDR_DEBUG_DELAY) can put
+// chosen waves to sleep; in the production build RN_DELAY is empty.
+#ifdef GDR_DEBUG_DELAY
+#define RN_DELAY() ::gdr::debug_delay()
+#else
+#define RN_DELAY() \
+  do {             \
+  } while (0)
+#endif
+#define RN_SYNC()    \
+  do {               \
+    __syncthreads(); \
+    RN_DELAY();      \
+  } while (0)
 
 constexpr int RN_GROUP = 32;          // workgroups per first-level group
 constexpr int RN_MAX_WG = 512;        // most workgroups (row partitions) per call
@@ -184,7 +203,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(sizeof(T) ==
     if constexpr (TPR == NT && NW > 1) {
       float* buf = s_red[red & 1];
       if ((tid & 63) == 0) buf[wv] = s;
-      __syncthreads();
+      RN_SYNC();
       s = buf[0];
 #pragma unroll
       for (int k = 1; k < NW; ++k) s += buf[k];
@@ -261,7 +280,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(sizeof(T) ==
 #pragma unroll
         for (int i = 0; i < 8; ++i) s_part[c + i] = dwp[8 * v + i];
     }
-    __syncthreads();
+    RN_SYNC();
   } else {
     for (int k = 0; k < NW; ++k) {
       if (wv == k) {
@@ -273,7 +292,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(sizeof(T) ==
             for (int i = 0; i < 8; ++i) s_part[c + i] = (k == 0 ? 0.f : s_part[c + i]) + dwp[8 * v + i];
         }
       }
-      __syncthreads();
+      RN_SYNC();
     }
   }
 
@@ -282,6 +301,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(sizeof(T) ==
     return;
   }
   float* mine = a.part + (long)g * N;
+  RN_DELAY();
   for (int c = 4 * tid; c < N; c += 4 * NT)
     *reinterpret_cast<f32x4*>(mine + c) = *reinterpret_cast<const f32x4*>(s_part + c);
   if (a.mode == GDR_REDUCE_SEPARATE) return;
@@ -293,24 +313,26 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(sizeof(T) ==
   const int grp = g / RN_GROUP;
   const int g0 = grp * RN_GROUP;
   const int members = min(RN_GROUP, a.G - g0);
-  __syncthreads();
+  RN_SYNC();
   if (tid == 0) {
     const unsigned prev = __hip_atomic_fetch_add(a.cnt + 1 + grp, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     s_last = prev == (unsigned)(members - 1);
   }
-  __syncthreads();
+  RN_SYNC();
   if (!s_last) return;
+  RN_DELAY();
   __threadfence();
   const int NG = (a.G + RN_GROUP - 1) / RN_GROUP;
   reduce_rows<NT, false>(a.part + (long)g0 * N, N, members, a.gpart + (long)grp * N);
-  __syncthreads();
+  RN_SYNC();
   if (tid == 0) {
     __hip_atomic_store(a.cnt + 1 + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const unsigned prev = __hip_atomic_fetch_add(a.cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     s_last = prev == (unsigned)(NG - 1);
   }
-  __syncthreads();
+  RN_SYNC();
   if (!s_last) return;
+  RN_DELAY();
   __threadfence();
   reduce_rows<NT, true>(a.gpart, N, NG, a.dw);
   if (tid == 0) __hip_atomic_store(a.cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -376,6 +398,15 @@ hipError_t launch_t(const RnArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+#ifdef GDR_DEBUG_DELAY
+namespace gdr {
+// the race-test build: this file's copy of the barrier-delay settings
+hipError_t debug_set_delay_rmsnorm(const DelayCfg& c) {
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_delay), &c, sizeof(c));
+}
+}  // namespace gdr
+#endif
 
 extern "C" {
 
