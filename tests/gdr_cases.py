@@ -29,7 +29,8 @@ TOL = {"f32": 1e-5, "bf16": 5e-3}
 # case, with the kernels as they stand.  The drawn cases set the larger
 # limits: rows of dh0 and 64-token blocks of dbeta / dg whose RMS is a few
 # times below the tensor's (strong decay with an initial state), and the
-# fp32 path's dg at the last token of a strongly decaying sequence.  The
+# fp32 path's dg at the last token of a strongly decaying sequence; the fp32
+# rows of o, dq, dk and dv are set by the 1000-token strong-decay cases.  The
 # bf16 rows are dominated by the rounding of outputs and MFMA operands to 8
 # significant bits (output rounding alone gives about 1.5e-2 of a row's RMS
 # at 10^5 rows; the worst rows of millions reach 4-9e-2), the fp32 ones by
@@ -43,7 +44,7 @@ EMAX_TOL = {
              "dh0": 2e-3},
 }
 ROW_TOL = {
-    "f32": {"o": 8e-5, "hT": 8e-5, "dq": 9e-5, "dk": 8e-5, "dv": 1e-4, "dbeta": 1.3e-4, "dg": 2e-4,
+    "f32": {"o": 1.2e-4, "hT": 8e-5, "dq": 1.5e-4, "dk": 1.5e-4, "dv": 1.3e-4, "dbeta": 1.3e-4, "dg": 2e-4,
             "dh0": 6e-5},
     "bf16": {"o": 3.5e-2, "hT": 6e-3, "dq": 9.5e-2, "dk": 1.2e-1, "dv": 1e-1, "dbeta": 3e-1, "dg": 1.2e-1,
              "dh0": 1.1e-1},

@@ -34,6 +34,13 @@ SMALL = {
     "bf16_short_T10": C[1].replace(name="bf16_T10", B=3, T=10, H=2, has_h0=True),
     "bf16_exact_T64": C[1].replace(name="bf16_T64", B=1, T=64, H=2, layout="VK", has_h0=True),
     "bf16_no_dhT": C[1].replace(name="bf16_no_dhT", B=1, T=130, H=2, has_dhT=False),
+    # the fp32 path over longer sequences: strong decay with an initial state,
+    # packed with 1- and 2-token sequences, and a two-sequence batch
+    "fp32_T1000_strong_decay": C[0].replace(name="fp32_T1000_strong", B=1, T=1000, H=2, DK=128, DV=128,
+                                            g_mean=-2.0, has_h0=True, layout="KV"),
+    "fp32_varlen_strong_decay": C[0].replace(name="fp32_varlen_strong", H=3, DK=128, DV=128,
+                                             lengths=[1, 500, 2, 700], g_mean=-2.0, has_h0=True, layout="KV"),
+    "fp32_B2_T2000": C[0].replace(name="fp32_T2000", B=2, T=2000, H=2, DK=64, DV=128, has_h0=True),
 }
 
 
