@@ -185,7 +185,7 @@ __global__ __launch_bounds__(256) void k_scan_bwd(const ScanBwdArgs a) {
 #pragma unroll
       for (int mt = 0; mt < MTH; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) store_acc4(db + acc_off(dkw / 16 + mt, dv0 / 16 + nt, DV), acc_h[mt][nt]);
+        for (int nt = 0; nt < NT; ++nt) store_acc4_nt(db + acc_off(dkw / 16 + mt, dv0 / 16 + nt, DV), acc_h[mt][nt]);
     }
     GDR_SYNC();  // dh^T complete; last chunk's readers of dDelta^T are done
     // dDelta = E (K dh) + scale P^T dO, rows 16w
@@ -202,7 +202,7 @@ __global__ __launch_bounds__(256) void k_scan_bwd(const ScanBwdArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       acc_d[nt] = acc_d[nt] * o.ee + (mtile ? zero4() : o.dl[nt]);
-      if constexpr (MODE != 0) store_acc4((T*)a.dD + ch * 64 * DV + acc_off(w, dv0 / 16 + nt, DV), acc_d[nt]);
+      if constexpr (MODE != 0) store_acc4_nt((T*)a.dD + ch * 64 * DV + acc_off(w, dv0 / 16 + nt, DV), acc_d[nt]);
       store_acc_t2(sDD, sDDl, LDD, rw, 16 * nt, -acc_d[nt]);
     }
     GDR_SYNC();  // -dDelta^T complete; all readers of dh^T are done

@@ -349,6 +349,23 @@ __device__ __forceinline__ void store_acc4(T* q, f32x4 v) {
   }
 }
 
+// store_acc4 with a non-temporal (streaming) store, for data that no other
+// workgroup of the same kernel reads and that the next kernel reads once
+// per tile: it then does not displace, in L2 and the Infinity Cache, the
+// chunk operands that several column tiles of a scan share.  Used for the
+// per-tile terms the WY passes hand to the scans (U; scale P^T dO, scale
+// Qg^T dO) and for the snapshots the scans hand to the gradient kernel.
+template <typename T>
+__device__ __forceinline__ void store_acc4_nt(T* q, f32x4 v) {
+  if constexpr (sizeof(T) == 2) {
+    typedef T t4 __attribute__((ext_vector_type(4)));
+    t4 w = {(T)v[0], (T)v[1], (T)v[2], (T)v[3]};
+    __builtin_nontemporal_store(w, reinterpret_cast<t4*>(q));
+  } else {
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(q));
+  }
+}
+
 // Store an accumulator tile in its own orientation: dst[(r0 + i) * ld + c0 + c].
 template <typename T>
 __device__ __forceinline__ void store_acc(T* dst, int64_t ld, int r0, int c0, f32x4 v) {

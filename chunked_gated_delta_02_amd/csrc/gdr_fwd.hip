@@ -318,7 +318,7 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
       }
       float* Ub = a.Ua + ch * 64 * DV;
 #pragma unroll
-      for (int nt = 0; nt < DVB / 16; ++nt) store_acc4(Ub + acc_off(w, dv0 / 16 + nt, DV), acc[nt]);
+      for (int nt = 0; nt < DVB / 16; ++nt) store_acc4_nt(Ub + acc_off(w, dv0 / 16 + nt, DV), acc[nt]);
     }
   }
 
@@ -397,9 +397,9 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
       float* Zb = a.Z + ch * DK * DV;
 #pragma unroll
       for (int nt = 0; nt < DVB / 16; ++nt) {
-        store_acc4(Db + acc_off(w, dv0 / 16 + nt, DV), accp[nt]);
+        store_acc4_nt(Db + acc_off(w, dv0 / 16 + nt, DV), accp[nt]);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) store_acc4(Zb + acc_off(w * MT + mt, dv0 / 16 + nt, DV), accz[mt][nt]);
+        for (int mt = 0; mt < MT; ++mt) store_acc4_nt(Zb + acc_off(w * MT + mt, dv0 / 16 + nt, DV), accz[mt][nt]);
       }
     }
   }
@@ -554,7 +554,7 @@ __global__ __launch_bounds__(MODE >= 2 ? 512 : 256) void k_scan_fwd(const ScanFw
 #pragma unroll
         for (int mt = 0; mt < MTH; ++mt)
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) store_acc4(hsb + acc_off(dkw / 16 + mt, dv0 / 16 + nt, DV), acc_h[mt][nt]);
+          for (int nt = 0; nt < NT; ++nt) store_acc4_nt(hsb + acc_off(dkw / 16 + mt, dv0 / 16 + nt, DV), acc_h[mt][nt]);
       }
     }
     GDR_SYNC();  // h^T of this chunk is complete
