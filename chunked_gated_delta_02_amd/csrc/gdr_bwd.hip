@@ -435,14 +435,16 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
         const int e = tid + 256 * q, ll = e & 63, tt = e >> 6;
         const int m = tt / NTB, nn = tt - m * NTB;
         const int64_t off = acc_off_l(m, dvb / 16 + nn, DV, ll);
-        hv[q] = load4f(hb + off);
-        gv[q] = *reinterpret_cast<const t4*>(db + off);
+        // the snapshots are read by this workgroup only: streaming loads
+        if constexpr (sizeof(HS) == 4) hv[q] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(hb + off));
+        else hv[q] = load4f(hb + off);
+        gv[q] = __builtin_nontemporal_load(reinterpret_cast<const t4*>(db + off));
       }
 #pragma unroll
       for (int q = 0; q < ID; ++q) {
         const int e = tid + 256 * q, ll = e & 63, tt = e >> 6;
         const int m = tt / NTB, nn = tt - m * NTB;
-        dv4[q] = *reinterpret_cast<const t4*>(ddb + acc_off_l(m, dvb / 16 + nn, DV, ll));
+        dv4[q] = __builtin_nontemporal_load(reinterpret_cast<const t4*>(ddb + acc_off_l(m, dvb / 16 + nn, DV, ll)));
       }
 #pragma unroll
       for (int q = 0; q < IH; ++q) {

@@ -246,7 +246,7 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = 4 * (tid + 256 * q);
-      *reinterpret_cast<f32x4*>(a.Tm + ch * 4096 + e) = *reinterpret_cast<const f32x4*>(sTm + (e >> 6) * LDF + (e & 63));
+      __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(sTm + (e >> 6) * LDF + (e & 63)), reinterpret_cast<f32x4*>(a.Tm + ch * 4096 + e));
     }
   }
 
@@ -525,8 +525,9 @@ __global__ __launch_bounds__(MODE >= 2 ? 512 : 256) void k_scan_fwd(const ScanFw
 #pragma unroll
         for (int ks = 0; ks < KS64; ++ks) o.x[KS + mt * KS64 + ks] = frag_af<T, 64>(Kb, dkw / 16 + mt, ks);
       const float* Ub = a.Ua + ch * 64 * DV;
+      // U is read by this tile only: streaming loads
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) o.v[nt] = *reinterpret_cast<const f32x4*>(Ub + acc_off(w, dv0 / 16 + nt, DV));
+      for (int nt = 0; nt < NT; ++nt) o.v[nt] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Ub + acc_off(w, dv0 / 16 + nt, DV)));
       o.v[NT] = *reinterpret_cast<const f32x4*>(gb + 128 + rw + acc_row0());
       o.s = gb[64 + 63];
     } else if constexpr (OUT) {
