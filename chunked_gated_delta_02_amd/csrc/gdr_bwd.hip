@@ -42,7 +42,10 @@ namespace gdr {
 // -dDelta^T goes to LDS as a split operand.  The per-chunk operands (K,
 // W^T, the two fp32 terms, the gate factors) are loaded raw into a ring of
 // SCAN_STAGES register sets, SCAN_STAGES - 1 chunks ahead; each chunk issues
-// the next loads in pieces between the MFMA steps of its dh update.  Writes the dh
+// the next loads in pieces spread over its step (K after the first barrier,
+// W^T after the K dh products, the fp32 terms and gates between the MFMA
+// steps of the dh update), so that the compute unit's memory pipeline, whose
+// issue rate bounds the step, drains between them.  Writes the dh
 // snapshot and dDelta (io dtype; the gradient kernel rounds its MFMA
 // operands to it anyway), both in accumulator order, and dh0.
 //   MODE 1: the reverse scan proper.
@@ -188,6 +191,11 @@ __global__ __launch_bounds__(256) void k_scan_bwd(const ScanBwdArgs a) {
         for (int nt = 0; nt < NT; ++nt) store_acc4_nt(db + acc_off(dkw / 16 + mt, dv0 / 16 + nt, DV), acc_h[mt][nt]);
     }
     GDR_SYNC();  // dh^T complete; last chunk's readers of dDelta^T are done
+    if (pf) {
+      __builtin_amdgcn_sched_barrier(0);
+      load_piece(cn, on, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // dDelta = E (K dh) + scale P^T dO, rows 16w
     f32x4 acc_d[NT];
 #pragma unroll
@@ -199,6 +207,11 @@ __global__ __launch_bounds__(256) void k_scan_bwd(const ScanBwdArgs a) {
         acc_d[nt] = Mma<T>::mma(o.kf[ks], frag_rowk(sDH, LDH, 16 * nt, ks * KW), acc_d[nt]);
         if constexpr (SPLIT) acc_d[nt] = Mma<T>::mma(o.kf[ks], frag_rowk(sDHl, LDH, 16 * nt, ks * KW), acc_d[nt]);
       }
+    if (pf) {
+      __builtin_amdgcn_sched_barrier(0);
+      load_piece(cn, on, 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       acc_d[nt] = acc_d[nt] * o.ee + (mtile ? zero4() : o.dl[nt]);
@@ -213,14 +226,14 @@ __global__ __launch_bounds__(256) void k_scan_bwd(const ScanBwdArgs a) {
       for (int nt = 0; nt < NT; ++nt) acc_h[mt][nt] = acc_h[mt][nt] * o.eL + (mtile ? zero4() : o.z[mt][nt]);
 #pragma unroll
     for (int ks = 0; ks < KS64; ++ks) {
-      // the prefetch is issued in pieces between these MFMA steps, where its
+      // the rest of the prefetch goes between these MFMA steps, where its
       // issue overlaps the MFMA chain instead of delaying the next barrier
       if (pf) {
         __builtin_amdgcn_sched_barrier(0);
         if (ks == 0) warm(c);
 #pragma unroll
-        for (int pc = 0; pc < 4; ++pc)
-          if (pc * KS64 / 4 == ks) load_piece(cn, on, pc);
+        for (int pc = 2; pc < 4; ++pc)
+          if ((pc - 2) * KS64 / 2 == ks) load_piece(cn, on, pc);
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll

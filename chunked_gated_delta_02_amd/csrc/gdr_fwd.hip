@@ -415,7 +415,13 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
 // that do not depend on h are loaded raw into a ring of SCAN_STAGES register
 // sets, SCAN_STAGES - 1 chunks ahead; nothing touches a loaded value before
 // its chunk is processed, so the loads stay in flight while earlier chunks
-// run.
+// run.  With the output fused and a ring of two or more stages, each role
+// issues its prefetch while the other role issues none: the recurrence waves
+// right after the first barrier (as the output waves form e^gamma Q h), the
+// output waves right after the second (as the recurrence waves update h).
+// The two roles' loads then do not queue behind each other in the compute
+// unit's memory pipeline, whose issue rate bounds the chunk step (the loads
+// for one chunk are ~68 KB per workgroup at 16-column tiles).
 //   MODE 2: 8 waves.  Waves 0..3 run the recurrence and write the
 //           snapshots; waves 4..7 compute o = scale (e^gamma (Q h) + P Delta)
 //           beside them from double-buffered copies of h^T and Delta^T, so
@@ -454,6 +460,7 @@ __global__ __launch_bounds__(MODE >= 2 ? 512 : 256) void k_scan_fwd(const ScanFw
   constexpr int NXR = KS + MTH * KS64;            // W, K^T
   constexpr int NXO = KS + (SPLIT ? 2 : 1) * KS64;  // Q, P (hi, lo)
   constexpr int NX = OUT ? cmax(NXR, NXO) : NXR;
+  constexpr bool LATE = OUT && S >= 2;   // prefetch issued inside the chunk step
   typedef typename Mma<T>::frag frag;
   constexpr int LDO = DVT + P;
   __shared__ __align__(16) T sH[NB][DVT * LDH];                   // h^T (dv, dk), hi
@@ -546,7 +553,9 @@ __global__ __launch_bounds__(MODE >= 2 ? 512 : 256) void k_scan_fwd(const ScanFw
     }
   };
 
-  auto process = [&](int c, Ops& o) {
+  // chunk c from stage o; with LATE and pf, the operands of chunk cn go to
+  // stage on from inside the step
+  auto process = [&](int c, Ops& o, int cn, Ops& on, bool pf) {
     const int64_t ch = chb + c;
     const int hb = OUT ? (c & 1) : 0;   // buffer holding h_c and Delta_c
     if constexpr (SNAP) {
@@ -561,6 +570,7 @@ __global__ __launch_bounds__(MODE >= 2 ? 512 : 256) void k_scan_fwd(const ScanFw
     GDR_SYNC();  // h^T of this chunk is complete
     f32x4 acc_o[NT];
     if (!orole) {
+      if (LATE && pf) load_ops(cn, on);   // (the output waves': after the next barrier)
       // Delta = U - W h (rows 16w)
       f32x4 acc_d[NT];
 #pragma unroll
@@ -594,6 +604,7 @@ __global__ __launch_bounds__(MODE >= 2 ? 512 : 256) void k_scan_fwd(const ScanFw
       for (int nt = 0; nt < NT; ++nt) acc_o[nt] *= o.v[NT];
     }
     GDR_SYNC();  // Delta^T complete; all readers of the other h^T buffer are done
+    if (LATE && pf && orole) load_ops(cn, on);
     if (!orole) {
       // h <- e^{gamma_L} h + K^T (E Delta)
 #pragma unroll
@@ -668,13 +679,14 @@ __global__ __launch_bounds__(MODE >= 2 ? 512 : 256) void k_scan_fwd(const ScanFw
     for (; cb + S <= nc; cb += S) {
 #pragma unroll
       for (int s = 0; s < S; ++s) {
-        load_ops(min(cb + s + S - 1, nc - 1), st[(s + S - 1) % S]);
-        process(cb + s, st[s]);
+        const int cn = min(cb + s + S - 1, nc - 1);
+        if (!LATE) load_ops(cn, st[(s + S - 1) % S]);
+        process(cb + s, st[s], cn, st[(s + S - 1) % S], true);
       }
     }
 #pragma unroll
     for (int s = 0; s < S - 1; ++s)
-      if (cb + s < nc) process(cb + s, st[s]);
+      if (cb + s < nc) process(cb + s, st[s], 0, st[s], false);
   }
   if (orole) return;
   if (MODE == 0) {
