@@ -145,12 +145,22 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
   const T* vp = (const T*)a.v;
   const int64_t rowq = (int64_t)t0 * H + h;   // token-row index of chunk row 0
 
+  // every input load is issued before the first wait (the gates by wave 0,
+  // then the K, Q and first V rows), so their latencies overlap; Q and V stay
+  // in registers until they are stored to LDS where needed
+  float gv = 0.f, bv = 0.f;
+  if (w == 0 && l < len) {
+    gv = a.g[(int64_t)(t0 + l) * H + h];
+    bv = a.beta[(int64_t)(t0 + l) * H + h];
+  }
+  RowBuf<T, DK> kbuf;
+  kbuf.load(kp + rowq * DK, (int64_t)H * DK, len);
+  RowBuf<T, DK> qbuf;
+  RowBuf<T, DVB> vbuf;
+  qbuf.load((const T*)a.q + rowq * DK, (int64_t)H * DK, len);
+  // first V block for U, or (backward without U) the first dO block
+  vbuf.load(BWD && !a.Ua ? (const T*)a.dO + rowq * DV : vp + rowq * DV, (int64_t)H * DV, len);
   if (w == 0) {
-    float gv = 0.f, bv = 0.f;
-    if (l < len) {
-      gv = a.g[(int64_t)(t0 + l) * H + h];
-      bv = a.beta[(int64_t)(t0 + l) * H + h];
-    }
     const float gm = wave_incl_scan(gv);
     const float gL = __shfl(gm, 63, 64);
     const float eg = expf(gm), eE = expf(gL - gm);
@@ -162,14 +172,7 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
     a.gam[ch * GSTRIDE + 64 + l] = eg;
     a.gam[ch * GSTRIDE + 128 + l] = eE;
   }
-  load_rows<T, DK>(sK, LDK, kp + rowq * DK, (int64_t)H * DK, len);
-  // the other inputs are fetched into registers now, so their latency
-  // overlaps the construction of T; each is stored to LDS when needed
-  RowBuf<T, DK> qbuf;
-  RowBuf<T, DVB> vbuf;
-  qbuf.load((const T*)a.q + rowq * DK, (int64_t)H * DK, len);
-  // first V block for U, or (backward without U) the first dO block
-  vbuf.load(BWD && !a.Ua ? (const T*)a.dO + rowq * DV : vp + rowq * DV, (int64_t)H * DV, len);
+  kbuf.store(sK, LDK);
   GDR_SYNC();
 
   // A = strictly_lower(diag(beta) K K^T * Gam): rows 16w, 4 column tiles
