@@ -424,7 +424,10 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
 // output waves right after the second (as the recurrence waves update h).
 // The two roles' loads then do not queue behind each other in the compute
 // unit's memory pipeline, whose issue rate bounds the chunk step (the loads
-// for one chunk are ~68 KB per workgroup at 16-column tiles).
+// for one chunk are ~68 KB per workgroup at 16-column tiles).  Without the
+// output role (MODE 0, 1) the prefetch goes in three pieces spread over the
+// step instead: W after the first barrier, K^T after the W h products, U and
+// the gates after the second barrier.
 //   MODE 2: 8 waves.  Waves 0..3 run the recurrence and write the
 //           snapshots; waves 4..7 compute o = scale (e^gamma (Q h) + P Delta)
 //           beside them from double-buffered copies of h^T and Delta^T, so
@@ -464,6 +467,7 @@ __global__ __launch_bounds__(MODE >= 2 ? 512 : 256) void k_scan_fwd(const ScanFw
   constexpr int NXO = KS + (SPLIT ? 2 : 1) * KS64;  // Q, P (hi, lo)
   constexpr int NX = OUT ? cmax(NXR, NXO) : NXR;
   constexpr bool LATE = OUT && S >= 2;   // prefetch issued inside the chunk step
+  constexpr bool SPREAD = !OUT && S >= 2;   // pieces spread over the step (no output role)
   typedef typename Mma<T>::frag frag;
   constexpr int LDO = DVT + P;
   __shared__ __align__(16) T sH[NB][DVT * LDH];                   // h^T (dv, dk), hi
@@ -522,6 +526,30 @@ __global__ __launch_bounds__(MODE >= 2 ? 512 : 256) void k_scan_fwd(const ScanFw
     f32x4 v[NT + 1];
     float s;
   };
+  // the recurrence's operands of load_ops in three pieces (W, K^T, U and the
+  // gates), for the spread prefetch of MODE 0 and 1
+  auto load_rpiece = [&](int c, Ops& o, int piece) {
+    const int64_t ch = chb + c;
+    const float* gb = a.gam + ch * GSTRIDE;
+    if (piece == 0) {
+      const T* Wb = (const T*)a.Wf + ch * 64 * DK;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) o.x[ks] = frag_af<T, DK>(Wb, w, ks);
+    } else if (piece == 1) {
+      const T* Kb = (const T*)a.KtTf + ch * DK * 64;
+#pragma unroll
+      for (int mt = 0; mt < MTH; ++mt)
+#pragma unroll
+        for (int ks = 0; ks < KS64; ++ks) o.x[KS + mt * KS64 + ks] = frag_af<T, 64>(Kb, dkw / 16 + mt, ks);
+    } else {
+      const float* Ub = a.Ua + ch * 64 * DV;
+      // U is read by this tile only: streaming loads
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) o.v[nt] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Ub + acc_off(w, dv0 / 16 + nt, DV)));
+      o.v[NT] = *reinterpret_cast<const f32x4*>(gb + 128 + rw + acc_row0());
+      o.s = gb[64 + 63];
+    }
+  };
   auto load_ops = [&](int c, Ops& o) {
     const int64_t ch = chb + c;
     const float* gb = a.gam + ch * GSTRIDE;
@@ -574,6 +602,7 @@ __global__ __launch_bounds__(MODE >= 2 ? 512 : 256) void k_scan_fwd(const ScanFw
     f32x4 acc_o[NT];
     if (!orole) {
       if (LATE && pf) load_ops(cn, on);   // (the output waves': after the next barrier)
+      if (SPREAD && pf) load_rpiece(cn, on, 0);
       // Delta = U - W h (rows 16w)
       f32x4 acc_d[NT];
 #pragma unroll
@@ -585,6 +614,7 @@ __global__ __launch_bounds__(MODE >= 2 ? 512 : 256) void k_scan_fwd(const ScanFw
           acc_d[nt] = Mma<T>::mma(o.x[ks], frag_rowk(sH[hb], LDH, 16 * nt, ks * KW), acc_d[nt]);
           if constexpr (SPLIT) acc_d[nt] = Mma<T>::mma(o.x[ks], frag_rowk(sHl[hb], LDH, 16 * nt, ks * KW), acc_d[nt]);
         }
+      if (SPREAD && pf) load_rpiece(cn, on, 1);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
@@ -609,6 +639,7 @@ __global__ __launch_bounds__(MODE >= 2 ? 512 : 256) void k_scan_fwd(const ScanFw
     GDR_SYNC();  // Delta^T complete; all readers of the other h^T buffer are done
     if (LATE && pf && orole) load_ops(cn, on);
     if (!orole) {
+      if (SPREAD && pf) load_rpiece(cn, on, 2);
       // h <- e^{gamma_L} h + K^T (E Delta)
 #pragma unroll
       for (int mt = 0; mt < MTH; ++mt)
@@ -683,7 +714,7 @@ __global__ __launch_bounds__(MODE >= 2 ? 512 : 256) void k_scan_fwd(const ScanFw
 #pragma unroll
       for (int s = 0; s < S; ++s) {
         const int cn = min(cb + s + S - 1, nc - 1);
-        if (!LATE) load_ops(cn, st[(s + S - 1) % S]);
+        if (!LATE && !SPREAD) load_ops(cn, st[(s + S - 1) % S]);
         process(cb + s, st[s], cn, st[(s + S - 1) % S], true);
       }
     }
