@@ -47,7 +47,10 @@ namespace gdr {
 // steps of the dh update), so that the compute unit's memory pipeline, whose
 // issue rate bounds the step, drains between them.  Writes the dh
 // snapshot and dDelta (io dtype; the gradient kernel rounds its MFMA
-// operands to it anyway), both in accumulator order, and dh0.
+// operands to it anyway), both in accumulator order, and dh0.  These two
+// are written with ordinary stores: the gradient kernel reads them right
+// after this kernel and finds them in the Infinity Cache (measured faster
+// than streaming stores, which leave the scan itself unchanged).
 //   MODE 1: the reverse scan proper.
 //   MODE 0: CP segment summary -- scans the augmented gradient [I | 0] of
 //           width DK + DV backwards over one segment (the identity columns
@@ -188,7 +191,7 @@ __global__ __launch_bounds__(256) void k_scan_bwd(const ScanBwdArgs a) {
 #pragma unroll
       for (int mt = 0; mt < MTH; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) store_acc4_nt(db + acc_off(dkw / 16 + mt, dv0 / 16 + nt, DV), acc_h[mt][nt]);
+        for (int nt = 0; nt < NT; ++nt) store_acc4(db + acc_off(dkw / 16 + mt, dv0 / 16 + nt, DV), acc_h[mt][nt]);
     }
     GDR_SYNC();  // dh^T complete; last chunk's readers of dDelta^T are done
     if (pf) {
@@ -215,7 +218,7 @@ __global__ __launch_bounds__(256) void k_scan_bwd(const ScanBwdArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       acc_d[nt] = acc_d[nt] * o.ee + (mtile ? zero4() : o.dl[nt]);
-      if constexpr (MODE != 0) store_acc4_nt((T*)a.dD + ch * 64 * DV + acc_off(w, dv0 / 16 + nt, DV), acc_d[nt]);
+      if constexpr (MODE != 0) store_acc4((T*)a.dD + ch * 64 * DV + acc_off(w, dv0 / 16 + nt, DV), acc_d[nt]);
       store_acc_t2(sDD, sDDl, LDD, rw, 16 * nt, -acc_d[nt]);
     }
     GDR_SYNC();  // -dDelta^T complete; all readers of dh^T are done
