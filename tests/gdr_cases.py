@@ -25,9 +25,10 @@ TOL = {"f32": 1e-5, "bf16": 5e-3}
 # to bound tightly).  The 0.1 rms floor keeps rows of near-zero reference
 # norm from dominating.  The limits are about twice the largest value
 # measured over every parity workload of the GPU tests (full-size workloads
-# 1-4 included), the 24 drawn cases of test_gpu_random.py and the smoke
-# case, with the kernels as they stand.  The drawn cases set the larger
-# limits: rows of dh0 and 64-token blocks of dbeta / dg whose RMS is a few
+# 1-4 included), a 200-case draw of test_gpu_random.py (GDR_RANDOM_CASES=200,
+# whose first 24 cases are the default draw; cases with fewer than 16
+# token-heads left out, see there) and the smoke case, with the kernels as
+# they stand.  The drawn cases set the larger limits: rows of dh0 and 64-token blocks of dbeta / dg whose RMS is a few
 # times below the tensor's (strong decay with an initial state), and the
 # fp32 path's dg at the last token of a strongly decaying sequence; the fp32
 # rows of o, dq, dk and dv are set by the 1000-token strong-decay cases.  The
@@ -38,15 +39,15 @@ TOL = {"f32": 1e-5, "bf16": 5e-3}
 # seen once it exceeds about a tenth of its row's RMS; smaller localized
 # defects are left to the bitwise GPU-vs-GPU tests.
 EMAX_TOL = {
-    "f32": {"o": 1e-5, "hT": 1e-5, "dq": 1e-5, "dk": 1e-5, "dv": 1.5e-5, "dbeta": 1.2e-5, "dg": 3e-5,
+    "f32": {"o": 1e-5, "hT": 2.7e-5, "dq": 1e-5, "dk": 3.1e-5, "dv": 3.3e-5, "dbeta": 3e-5, "dg": 3e-5,
             "dh0": 1e-5},
-    "bf16": {"o": 8e-3, "hT": 1.5e-3, "dq": 1e-2, "dk": 9e-3, "dv": 1.2e-2, "dbeta": 1.3e-2, "dg": 1.2e-2,
+    "bf16": {"o": 8e-3, "hT": 1.5e-3, "dq": 1.2e-2, "dk": 1e-2, "dv": 1.2e-2, "dbeta": 1.3e-2, "dg": 1.2e-2,
              "dh0": 2e-3},
 }
 ROW_TOL = {
-    "f32": {"o": 1.2e-4, "hT": 8e-5, "dq": 1.5e-4, "dk": 1.5e-4, "dv": 1.3e-4, "dbeta": 1.3e-4, "dg": 2e-4,
+    "f32": {"o": 1.5e-4, "hT": 1.7e-4, "dq": 2.1e-4, "dk": 1.5e-4, "dv": 1.5e-4, "dbeta": 2e-4, "dg": 3e-4,
             "dh0": 6e-5},
-    "bf16": {"o": 3.5e-2, "hT": 6e-3, "dq": 9.5e-2, "dk": 1.2e-1, "dv": 1e-1, "dbeta": 3e-1, "dg": 1.2e-1,
+    "bf16": {"o": 3.5e-2, "hT": 6e-3, "dq": 1e-1, "dk": 1.2e-1, "dv": 1e-1, "dbeta": 4e-1, "dg": 2.5e-1,
              "dh0": 1.1e-1},
 }
 OUTS_FWD = ("o", "hT")

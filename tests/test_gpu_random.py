@@ -6,6 +6,8 @@ dtype, context-parallel segments and the decay regime.  The draws come from
 one seeded NumPy generator, so the cases are the same on every run; each is
 held to the same normwise, max-element and row bounds as the named
 workloads."""
+import os
+
 import numpy as np
 import pytest
 
@@ -14,13 +16,16 @@ from tests.gdr_cases import compare, run_gpu, run_oracle, say
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 24
+# 24 by default; GDR_RANDOM_CASES=N draws a longer sweep (the first 24 cases
+# are the same either way)
+N_DEFAULT = 24
+N_CASES = int(os.environ.get("GDR_RANDOM_CASES", N_DEFAULT))
 
 
-def _draw_cases():
+def _draw_cases(n=None):
     rng = np.random.default_rng(2026)
     cases = []
-    for i in range(N_CASES):
+    for i in range(N_CASES if n is None else n):
         io = "f32" if rng.random() < 0.25 else "bf16"
         DK = int(rng.choice([64, 128]))
         DV = int(rng.choice([64, 128, 192, 256]))
@@ -49,10 +54,13 @@ def _draw_cases():
 CASES = _draw_cases()
 
 
+def _token_heads(w):
+    return (sum(w.lengths) if w.lengths is not None else w.B * w.T) * w.H
+
+
 def _one_element_dg(w):
     # one token of one head: dg is a single number
-    tokens = sum(w.lengths) if w.lengths is not None else w.B * w.T
-    return tokens * w.H == 1
+    return _token_heads(w) == 1
 
 
 # On the bf16 path the gradient kernel takes the fp32 state as one bf16
@@ -63,12 +71,30 @@ def _one_element_dg(w):
 # the 5e-3 bound the workloads state for their tensors of thousands of
 # elements.  Every other output of the case, and its element-wise bounds,
 # pass.
-_XFAIL_ONE = pytest.mark.xfail(strict=True, reason="one-element dg: bf16 rounding of the state operand in the "
-                                                    "gradient kernel exceeds the normwise bound on a single element")
+_REASON = "one-element dg: bf16 rounding of the state operand in the gradient kernel can exceed the normwise bound " \
+          "on a single element"
 
 
-@pytest.mark.parametrize("i", [pytest.param(i, marks=_XFAIL_ONE) if _one_element_dg(CASES[i]) else i
-                               for i in range(N_CASES)])
+# The same holds for any output of a handful of elements: in a longer sweep
+# a single token of four heads (no initial state) gave a normwise dbeta error
+# of 6.6e-3 over its 4 elements, and rounding dh_T alone to bf16 in the
+# oracle moves it by 6.3e-3 (tests/test_single_token_sensitivity.py).  Cases
+# of fewer than 16 token-heads beyond the default draw may therefore fail.
+_REASON_TINY = "fewer than 16 token-heads: bf16 rounding of the state and state-gradient operands can exceed the " \
+               "normwise bound on a handful of elements"
+
+
+def _param(i):
+    w = CASES[i]
+    if i < N_DEFAULT:
+        # the default set's one-element case is known to exceed the bound
+        return pytest.param(i, marks=pytest.mark.xfail(strict=True, reason=_REASON)) if _one_element_dg(w) else i
+    if _token_heads(w) < 16:
+        return pytest.param(i, marks=pytest.mark.xfail(strict=False, reason=_REASON_TINY))
+    return i
+
+
+@pytest.mark.parametrize("i", [_param(i) for i in range(N_CASES)])
 def test_random_case_matches_oracle(i):
     w = CASES[i]
     say("[case] %s: %s" % (w.name, w))
