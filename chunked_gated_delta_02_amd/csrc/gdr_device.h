@@ -354,11 +354,13 @@ __device__ __forceinline__ void store_acc4(T* q, f32x4 v) {
 // it then does not displace, in L2 and the Infinity Cache, the chunk
 // operands that several column tiles of a scan share.  Used for the
 // per-tile terms the WY passes hand to the scans (U; scale P^T dO, scale
-// Qg^T dO) and for the snapshots the scans hand to the gradient kernel; the
-// backward WY pass stores T the same way, and the readers of these buffers
-// load them with non-temporal loads as well.  (The shared W, K^T, Q, P and
-// W^T, K fragments keep ordinary stores and loads: loading them
-// non-temporally made the forward scan 27 us slower.)
+// Qg^T dO) and for the forward's state snapshots; the backward WY pass
+// stores T the same way, and the readers of these buffers load them with
+// non-temporal loads as well.  (The shared W, K^T, Q, P and W^T, K
+// fragments keep ordinary stores and loads: loading them non-temporally
+// made the forward scan 27 us slower.  The reverse scan's dh snapshots and
+// dDelta keep ordinary stores too: the gradient kernel, which runs right
+// after it, then finds them in the Infinity Cache.)
 template <typename T>
 __device__ __forceinline__ void store_acc4_nt(T* q, f32x4 v) {
   if constexpr (sizeof(T) == 2) {
