@@ -427,7 +427,12 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
 // for one chunk are ~68 KB per workgroup at 16-column tiles).  Without the
 // output role (MODE 0, 1) the prefetch goes in three pieces spread over the
 // step instead: W after the first barrier, K^T after the W h products, U and
-// the gates after the second barrier.
+// the gates after the second barrier.  With the output fused, each role
+// runs a chunk loop of its own, chosen by a wave-uniform branch: the
+// compiler's memory-wait analysis then sees only the role's own loads (with
+// one loop for both, its paths ran the output waves' loads into the
+// recurrence's registers and it waited for every load before the state
+// update).
 //   MODE 2: 8 waves.  Waves 0..3 run the recurrence and write the
 //           snapshots; waves 4..7 compute o = scale (e^gamma (Q h) + P Delta)
 //           beside them from double-buffered copies of h^T and Delta^T, so
@@ -488,7 +493,7 @@ __global__ __launch_bounds__(MODE >= 2 ? 512 : 256) void k_scan_fwd(const ScanFw
   const int dv0 = MODE == 0 ? (mtile ? 0 : col0 - DK) : col0;   // column of U (and o)
   int c0, nc, ts, tl;
   seg_range(a.geo, n, sg, c0, nc, ts, tl);
-  const bool orole = OUT && wave_id() >= 4;   // output waves
+  const bool orole = OUT && __builtin_amdgcn_readfirstlane(wave_id()) >= 4;   // output waves (wave-uniform)
   const int w = wave_id() & 3;                // row block of either role
   const int l = lane_id();
   const int dkw = w * (DK / 4);
@@ -550,10 +555,11 @@ __global__ __launch_bounds__(MODE >= 2 ? 512 : 256) void k_scan_fwd(const ScanFw
       o.s = gb[64 + 63];
     }
   };
-  auto load_ops = [&](int c, Ops& o) {
+  auto load_ops = [&](auto role, int c, Ops& o) {
+    constexpr bool OR = decltype(role)::value;
     const int64_t ch = chb + c;
     const float* gb = a.gam + ch * GSTRIDE;
-    if (!orole) {
+    if constexpr (!OR) {
       const T* Wb = (const T*)a.Wf + ch * 64 * DK;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) o.x[ks] = frag_af<T, DK>(Wb, w, ks);
@@ -586,11 +592,12 @@ __global__ __launch_bounds__(MODE >= 2 ? 512 : 256) void k_scan_fwd(const ScanFw
 
   // chunk c from stage o; with LATE and pf, the operands of chunk cn go to
   // stage on from inside the step
-  auto process = [&](int c, Ops& o, int cn, Ops& on, bool pf) {
+  auto process = [&](auto role, int c, Ops& o, int cn, Ops& on, bool pf) {
+    constexpr bool OR = decltype(role)::value;
     const int64_t ch = chb + c;
     const int hb = OUT ? (c & 1) : 0;   // buffer holding h_c and Delta_c
     if constexpr (SNAP) {
-      if (!orole) {
+      if constexpr (!OR) {
         HS* hsb = (HS*)a.hs + ch * DK * DV;
 #pragma unroll
         for (int mt = 0; mt < MTH; ++mt)
@@ -600,8 +607,12 @@ __global__ __launch_bounds__(MODE >= 2 ? 512 : 256) void k_scan_fwd(const ScanFw
     }
     GDR_SYNC();  // h^T of this chunk is complete
     f32x4 acc_o[NT];
-    if (!orole) {
-      if (LATE && pf) load_ops(cn, on);   // (the output waves': after the next barrier)
+    if constexpr (!OR) {
+      if (LATE && pf) {   // (the output waves': after the next barrier)
+        __builtin_amdgcn_sched_barrier(0);
+        load_ops(role, cn, on);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       if (SPREAD && pf) load_rpiece(cn, on, 0);
       // Delta = U - W h (rows 16w)
       f32x4 acc_d[NT];
@@ -637,8 +648,14 @@ __global__ __launch_bounds__(MODE >= 2 ? 512 : 256) void k_scan_fwd(const ScanFw
       for (int nt = 0; nt < NT; ++nt) acc_o[nt] *= o.v[NT];
     }
     GDR_SYNC();  // Delta^T complete; all readers of the other h^T buffer are done
-    if (LATE && pf && orole) load_ops(cn, on);
-    if (!orole) {
+    if constexpr (OR) {
+      if (LATE && pf) {
+        __builtin_amdgcn_sched_barrier(0);
+        load_ops(role, cn, on);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if constexpr (!OR) {
       if (SPREAD && pf) load_rpiece(cn, on, 2);
       // h <- e^{gamma_L} h + K^T (E Delta)
 #pragma unroll
@@ -705,23 +722,29 @@ __global__ __launch_bounds__(MODE >= 2 ? 512 : 256) void k_scan_fwd(const ScanFw
   // a prefetch and its use is then fixed, and the compiler's wait counts let
   // the prefetched loads stay in flight.  A static tail runs the last
   // nc % S chunks.
-  if (nc > 0) {
-    Ops st[S];
+  // each role runs a loop of its own (the same barriers, in the same order),
+  // selected by a wave-uniform branch
+  auto run = [&](auto role) {
+    if (nc > 0) {
+      Ops st[S];
 #pragma unroll
-    for (int s = 0; s < S - 1; ++s) load_ops(min(s, nc - 1), st[s]);
-    int cb = 0;
-    for (; cb + S <= nc; cb += S) {
+      for (int s = 0; s < S - 1; ++s) load_ops(role, min(s, nc - 1), st[s]);
+      int cb = 0;
+      for (; cb + S <= nc; cb += S) {
 #pragma unroll
-      for (int s = 0; s < S; ++s) {
-        const int cn = min(cb + s + S - 1, nc - 1);
-        if (!LATE && !SPREAD) load_ops(cn, st[(s + S - 1) % S]);
-        process(cb + s, st[s], cn, st[(s + S - 1) % S], true);
+        for (int s = 0; s < S; ++s) {
+          const int cn = min(cb + s + S - 1, nc - 1);
+          if (!LATE && !SPREAD) load_ops(role, cn, st[(s + S - 1) % S]);
+          process(role, cb + s, st[s], cn, st[(s + S - 1) % S], true);
+        }
       }
-    }
 #pragma unroll
-    for (int s = 0; s < S - 1; ++s)
-      if (cb + s < nc) process(cb + s, st[s], 0, st[s], false);
-  }
+      for (int s = 0; s < S - 1; ++s)
+        if (cb + s < nc) process(role, cb + s, st[s], 0, st[s], false);
+    }
+  };
+  if (OUT && orole) run(std::integral_constant<bool, OUT>{});
+  else run(std::false_type{});
   if (orole) return;
   if (MODE == 0) {
 #pragma unroll
