@@ -19,7 +19,10 @@ typedef __bf16 bf16;
 #define GDR_LDS __attribute__((address_space(3)))
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
-__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+// wave index within the workgroup, as a wave-uniform (scalar) value: the
+// compiler then keeps it and what is derived from it in scalar registers and
+// branches on it without execution masks
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // ---------------------------------------------------------------------------
 // element conversions

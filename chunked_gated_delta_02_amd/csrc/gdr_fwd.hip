@@ -493,7 +493,7 @@ __global__ __launch_bounds__(MODE >= 2 ? 512 : 256) void k_scan_fwd(const ScanFw
   const int dv0 = MODE == 0 ? (mtile ? 0 : col0 - DK) : col0;   // column of U (and o)
   int c0, nc, ts, tl;
   seg_range(a.geo, n, sg, c0, nc, ts, tl);
-  const bool orole = OUT && __builtin_amdgcn_readfirstlane(wave_id()) >= 4;   // output waves (wave-uniform)
+  const bool orole = OUT && wave_id() >= 4;   // output waves (wave-uniform)
   const int w = wave_id() & 3;                // row block of either role
   const int l = lane_id();
   const int dkw = w * (DK / 4);
