@@ -462,10 +462,10 @@ __global__ __launch_bounds__(MODE >= 2 ? 512 : 256) void k_scan_fwd(const ScanFw
   constexpr int MTH = DK / 64;
   constexpr int NT = DVT / 16;
   constexpr int NB = OUT ? 2 : 1;   // h^T / Delta^T buffers
-  // fp32 fragments are 8x larger: shallower ring; 32-column output and
-  // snapshot tiles take 2 stages and 64-column output tiles 1, so that two
-  // waves fit on each SIMD
-  constexpr int S = sizeof(T) == 2 ? (OUT && DVT == 64 ? 1 : ((OUT && DVT == 32) || (MODE == 1 && DVT == 32) ? 2 : SCAN_STAGES))
+  // fp32 fragments are 8x larger: shallower ring; 32-column snapshot tiles
+  // take 2 stages and 64-column output tiles 2, so that two waves fit on
+  // each SIMD
+  constexpr int S = sizeof(T) == 2 ? ((OUT && DVT == 64) || (MODE == 1 && DVT == 32) ? 2 : SCAN_STAGES)
                                    : (OUT ? 1 : 2);
   // raw operand slots per ring stage, shared by both roles
   constexpr int NXR = KS + MTH * KS64;            // W, K^T
