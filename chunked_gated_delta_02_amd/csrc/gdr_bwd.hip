@@ -335,11 +335,12 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
   constexpr int PH2 = (2 * 64 * LDK + DK * L64 + 64 * L64) * (int)sizeof(T);
   extern __shared__ __align__(16) char smem[];
   T* sT = (T*)smem;                       // T (r, s), operand copy
-  float* sg = (float*)(sT + 64 * L64);    // gamma * log2(e)
+  float* sg = (float*)(sT + 64 * L64);    // gamma (hi)
   float* sb = sg + 64;                    // beta
   float* seg = sb + 64;                   // e^gamma
   float* sE = seg + 64;                   // e^{gamma_L - gamma}
-  float* sRed = sE + 64;                  // [2][4][64] column-sum partials
+  float* sgl = sE + 64;                   // gamma (lo)
+  float* sRed = sgl + 64;                 // [2][4][64] column-sum partials
   float* sMisc = sRed + 2 * 4 * 64;       // [8]: per-wave gamma_L partials
   char* uni = (char*)(sMisc + 8);
   // phase 1
@@ -370,7 +371,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
   const float scale = a.scale;
 
   if (tid < 64) {
-    sg[tid] = a.gam[ch * GSTRIDE + tid] * LOG2E;
+    sg[tid] = a.gam[ch * GSTRIDE + tid];
+    sgl[tid] = a.gaml[ch * 64 + tid];
     sb[tid] = (tid < len) ? a.beta[(int64_t)(t0 + tid) * H + h] : 0.f;
     seg[tid] = a.gam[ch * GSTRIDE + 64 + tid];
     sE[tid] = a.gam[ch * GSTRIDE + 128 + tid];
@@ -573,7 +575,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
   // per-column gate values are read from LDS where they are used
   auto gam = [&](int nt, int i) {
     const int r = r0 + i, s = 16 * nt + acc_col();
-    const float e = exp2_hw(sg[r] - sg[s]);
+    const float e = gate_factor<sizeof(T) == 4>(sg, sgl, r, s);
     return (s <= r) ? e : 0.f;
   };
   // dP (scaled, masked) and dQK = dP * Gam -> LDS as (dP * Gam)^T
@@ -754,7 +756,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
         const int r = r0 + i, s = 16 * nt + acc_col();
         float gv = 0.f;
         if (s < r) {
-          const float Gm = exp2_hw(sg[r] - sg[s]);
+          const float Gm = gate_factor<sizeof(T) == 4>(sg, sgl, r, s);
           const float dA = -aA[nt][i];
           rb[i] += dA * aKK[nt][i] * Gm;
           const float X = dA * sb[r] * aKK[nt][i] * Gm;
@@ -830,7 +832,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_grad(const Grad
                   sRed[1 * 256 + 3 * 64 + l]);
     if (l == 63) {
       // gamma_L terms: e^{gamma_L} <dh, h> and sum_r E_r rowsum(K * Delta dh^T)
-      dgam += exp2_hw(sg[63]) * (sMisc[0] + sMisc[1] + sMisc[2] + sMisc[3]) +
+      dgam += seg[63] * (sMisc[0] + sMisc[1] + sMisc[2] + sMisc[3]) +
               (sMisc[4] + sMisc[5] + sMisc[6] + sMisc[7]);
     }
     const float dgv = wave_suffix_scan(dgam);
@@ -874,7 +876,7 @@ static size_t grad_smem() {
   constexpr int LDK = DK + P, L64 = 64 + P, DVB = GRAD_DVB, LDV = DVB + P;
   constexpr int PH1 = (2 * DVB * LDK + 3 * DVB * L64 + 64 * LDV + DK * L64) * (int)sizeof(T);
   constexpr int PH2 = (2 * 64 * LDK + DK * L64 + 64 * L64) * (int)sizeof(T);
-  return 64 * L64 * sizeof(T) + (4 * 64 + 2 * 4 * 64 + 8) * 4 + cmax(PH1, PH2);
+  return 64 * L64 * sizeof(T) + (5 * 64 + 2 * 4 * 64 + 8) * 4 + cmax(PH1, PH2);
 }
 
 template <typename T, typename HS, int DK>

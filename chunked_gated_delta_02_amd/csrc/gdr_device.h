@@ -384,15 +384,51 @@ __device__ __forceinline__ void store_acc(T* dst, int64_t ld, int r0, int c0, f3
 }
 
 // ---------------------------------------------------------------------------
-// Gate factors.  Kernels keep gamma in LDS pre-multiplied by log2(e), so a
-// factor exp(gamma_r - gamma_s) is one hardware 2^x (v_exp_f32) of a
-// difference; the extra rounding (about |gamma| * 2^-24 relative) is of the
-// order of the cumulative sum's own.
+// Gate factors.  The chunk-local cumulative sum gamma is formed exactly as a
+// pair of floats (hi + lo, error-free two-sum additions in the wave scan).
+// A factor exp(gamma_r - gamma_s) is one
+// hardware 2^x (v_exp_f32) of ((hi_r - hi_s) + (lo_r - lo_s)) log2(e): the
+// difference is taken before anything is rounded at the scale of gamma
+// itself.  With fast decay (gamma of -100 and more at the end of a chunk) an
+// fp32 cumulative sum, or gamma scaled by log2(e) before the difference,
+// would put errors of ~1e-5 relative into factors near 1.
 constexpr float LOG2E = 1.4426950408889634f;
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+// exp(gamma_r - gamma_s) from the hi / lo arrays of gamma.  The lo part is
+// used on the fp32 path only: on the bf16 path the factors enter products
+// whose operands are rounded to 8 bits, so the hi difference (relative
+// error ~|gamma| 2^-24) is ample and saves the extra LDS reads and VALU work.
+template <bool EXACT>
+__device__ __forceinline__ float gate_factor(const float* hi, const float* lo, int r, int s) {
+  if constexpr (EXACT) return exp2_hw(((hi[r] - hi[s]) + (lo[r] - lo[s])) * LOG2E);
+  else return exp2_hw((hi[r] - hi[s]) * LOG2E);
+}
 
 // ---------------------------------------------------------------------------
 // Wavefront scans over 64 lanes.
+// inclusive scan in float pairs (hi + lo): each addition's rounding error is
+// recovered exactly (Knuth's two-sum) and carried in lo, so hi + lo is the
+// sum to about 2^-48 relative
+__device__ __forceinline__ float wave_incl_scan_2f(float x, float& lo_out) {
+  const int l = lane_id();
+  float hi = x, lo = 0.f;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const float yh = __shfl_up(hi, d, 64), yl = __shfl_up(lo, d, 64);
+    if (l >= d) {
+      const float sh = hi + yh;
+      const float bb = sh - hi;
+      const float err = (hi - (sh - bb)) + (yh - bb);
+      hi = sh;
+      lo = lo + yl + err;
+      const float t = hi + lo;
+      lo = lo - (t - hi);
+      hi = t;
+    }
+  }
+  lo_out = lo;
+  return hi;
+}
 __device__ __forceinline__ float wave_incl_scan(float x) {
   const int l = lane_id();
 #pragma unroll

@@ -130,10 +130,11 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
   T* sVu = (T*)r2;                        // V block (r, dv) of U
   T* sQ = (T*)r2;                         // Q (r, dk)
   T* sVd = sK;                            // dO block (r, dv) (backward, after P^T)
-  float* sg = (float*)(r2 + R2);
+  float* sg = (float*)(r2 + R2);          // gamma (hi)
   float* sb = sg + 64;
   float* seg = sb + 64;
   float* sE = seg + 64;
+  float* sgl = sE + 64;                   // gamma (lo)
 
   const int ci = blockIdx.x, h = blockIdx.y;
   int n, t0, len;
@@ -161,16 +162,22 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
   // first V block for U, or (backward without U) the first dO block
   vbuf.load(BWD && !a.Ua ? (const T*)a.dO + rowq * DV : vp + rowq * DV, (int64_t)H * DV, len);
   if (w == 0) {
-    const float gm = wave_incl_scan(gv);
-    const float gL = __shfl(gm, 63, 64);
-    const float eg = expf(gm), eE = expf(gL - gm);
-    sg[l] = gm * LOG2E;
+    // gamma as hi + lo (two-sum scan); e^{gamma_L - gamma} from the exact
+    // difference (e^gamma needs none: gamma's own rounding is relative to
+    // gamma, and e^gamma is negligible wherever gamma is large)
+    float glo;
+    const float ghi = wave_incl_scan_2f(gv, glo);
+    const float gLh = __shfl(ghi, 63, 64), gLl = __shfl(glo, 63, 64);
+    const float eg = exp2_hw(ghi * LOG2E), eE = exp2_hw(((gLh - ghi) + (gLl - glo)) * LOG2E);
+    sg[l] = ghi;
+    sgl[l] = glo;
     sb[l] = bv;
     seg[l] = eg;
     sE[l] = eE;
-    a.gam[ch * GSTRIDE + l] = gm;
+    a.gam[ch * GSTRIDE + l] = ghi;
     a.gam[ch * GSTRIDE + 64 + l] = eg;
     a.gam[ch * GSTRIDE + 128 + l] = eE;
+    a.gaml[ch * 64 + l] = glo;
   }
   kbuf.store(sK, LDK);
   GDR_SYNC();
@@ -191,7 +198,7 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * w + acc_row0() + i, s = 16 * nt + acc_col();
-        sA[r * LDF + s] = (s < r) ? sb[r] * acc[nt][i] * exp2_hw(sg[r] - sg[s]) : 0.f;
+        sA[r * LDF + s] = (s < r) ? sb[r] * acc[nt][i] * gate_factor<sizeof(T) == 4>(sg, sgl, r, s) : 0.f;
       }
   }
   GDR_SYNC();
@@ -348,7 +355,7 @@ __global__ __launch_bounds__(256) void k_wy(const WyArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int x = 16 * w + acc_row0() + i, y = 16 * nt + acc_col();
         const int r = BWD ? y : x, s = BWD ? x : y;
-        acc[nt][i] = (s <= r) ? acc[nt][i] * exp2_hw(sg[r] - sg[s]) : 0.f;
+        acc[nt][i] = (s <= r) ? acc[nt][i] * gate_factor<sizeof(T) == 4>(sg, sgl, r, s) : 0.f;
       }
       store_acc(sPT, LDF, 16 * w, 16 * nt, acc[nt]);
     }
@@ -859,7 +866,7 @@ static size_t wy_smem() {
   constexpr int P = pad_of<T>();
   constexpr int LDK = DK + P, LDF = 68, DVB = dvb_of<T>(), LDV = DVB + P;
   constexpr int R2 = cmax(64 * LDK * (int)sizeof(T), cmax(64 * LDV * (int)sizeof(T), 4 * 16 * 20 * 4));
-  return 64 * LDK * sizeof(T) + 64 * LDF * 4 + R2 + 4 * 64 * 4;
+  return 64 * LDK * sizeof(T) + 64 * LDF * 4 + R2 + 5 * 64 * 4;
 }
 
 template <typename T, int DK, bool BWD>

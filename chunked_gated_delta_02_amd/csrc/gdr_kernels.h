@@ -7,8 +7,10 @@
 
 #define GDR_MAX_SEQS 8192
 
-// per chunk-head gate block in the workspace: gamma[64], e^gamma[64],
-// e^{gamma_L - gamma}[64]
+// per chunk-head gate block in the workspace: gamma[64] (hi), e^gamma[64],
+// e^{gamma_L - gamma}[64]; the lo part of gamma (gamma = hi + lo, an exact
+// two-float sum) lives in an array of its own, 64 per chunk-head, at the end
+// of the workspace
 #define GSTRIDE 192
 
 
@@ -42,7 +44,8 @@ struct WyArgs {
   const void* dO;    // backward only
   const float* beta;
   const float* g;
-  float* gam;   // [GSTRIDE]: gamma, e^gamma, e^{gamma_L - gamma}
+  float* gam;   // [GSTRIDE]: gamma (hi), e^gamma, e^{gamma_L - gamma}
+  float* gaml;  // [64]: gamma (lo)
   void* Wf;     // afrag<64, DK>: W (rows r, k = dk); backward: nullable
   float* Ua;    // acc<64, DV> fp32: U; backward: nullable
   void* KtTf;   // afrag<DK, 64>: K^T (exact; nullable)
@@ -123,6 +126,7 @@ struct GradArgs {
   const void* dO;
   const float* beta;
   const float* gam;
+  const float* gaml;    // [64] per chunk-head: gamma (lo)
   const void* WTf;      // afrag<DK, 64>: W^T
   const float* Tm;      // [64][64] row-major fp32: T
   const void* hs;
