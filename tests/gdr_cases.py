@@ -37,16 +37,19 @@ TOL = {"f32": 1e-5, "bf16": 5e-3}
 # at 10^5 rows; the worst rows of millions reach 4-9e-2), the fp32 ones by
 # accumulation order.  So on the bf16 path an error confined to a few rows is
 # seen once it exceeds about a tenth of its row's RMS; smaller localized
-# defects are left to the bitwise GPU-vs-GPU tests.
+# defects are left to the bitwise GPU-vs-GPU tests.  The fp32 limits were
+# re-derived once gamma became an exact two-float sum (fast decay had set the
+# old ones): about twice the largest values over every GPU test and a
+# 3000-case draw of test_gpu_random.py, the three cases named there left out.
 EMAX_TOL = {
-    "f32": {"o": 1e-5, "hT": 2.7e-5, "dq": 1e-5, "dk": 3.1e-5, "dv": 3.3e-5, "dbeta": 3e-5, "dg": 3e-5,
-            "dh0": 1e-5},
+    "f32": {"o": 4e-6, "hT": 2e-6, "dq": 5e-6, "dk": 5e-6, "dv": 2e-6, "dbeta": 1e-5, "dg": 1.2e-5,
+            "dh0": 2e-6},
     "bf16": {"o": 8e-3, "hT": 1.5e-3, "dq": 1.2e-2, "dk": 1e-2, "dv": 1.2e-2, "dbeta": 1.3e-2, "dg": 1.2e-2,
              "dh0": 2e-3},
 }
 ROW_TOL = {
-    "f32": {"o": 1.5e-4, "hT": 1.7e-4, "dq": 2.1e-4, "dk": 1.5e-4, "dv": 1.5e-4, "dbeta": 2e-4, "dg": 3e-4,
-            "dh0": 6e-5},
+    "f32": {"o": 5e-5, "hT": 1.2e-5, "dq": 6e-5, "dk": 5e-5, "dv": 4e-5, "dbeta": 7e-5, "dg": 6e-4,
+            "dh0": 1e-5},
     "bf16": {"o": 3.5e-2, "hT": 6e-3, "dq": 1e-1, "dk": 1.2e-1, "dv": 1e-1, "dbeta": 4e-1, "dg": 2.5e-1,
              "dh0": 1.1e-1},
 }
