@@ -41,6 +41,10 @@ TOL = {"f32": 1e-5, "bf16": 5e-3}
 # re-derived once gamma became an exact two-float sum (fast decay had set the
 # old ones): about twice the largest values over every GPU test and a
 # 3000-case draw of test_gpu_random.py, the three cases named there left out.
+# A 6000-case draw then set the bf16 dbeta and dg row limits: its largest
+# 64-token blocks reached 0.41 and 0.30 of their rows' RMS (short outputs
+# whose blocks carry the bf16 rounding of the state-gradient operand), so
+# those two limits are about 1.3 times that.
 EMAX_TOL = {
     "f32": {"o": 4e-6, "hT": 2e-6, "dq": 5e-6, "dk": 5e-6, "dv": 2e-6, "dbeta": 1e-5, "dg": 1.2e-5,
             "dh0": 2e-6},
@@ -50,7 +54,7 @@ EMAX_TOL = {
 ROW_TOL = {
     "f32": {"o": 5e-5, "hT": 1.2e-5, "dq": 6e-5, "dk": 5e-5, "dv": 4e-5, "dbeta": 7e-5, "dg": 6e-4,
             "dh0": 1e-5},
-    "bf16": {"o": 3.5e-2, "hT": 6e-3, "dq": 1e-1, "dk": 1.2e-1, "dv": 1e-1, "dbeta": 4e-1, "dg": 2.5e-1,
+    "bf16": {"o": 3.5e-2, "hT": 6e-3, "dq": 1e-1, "dk": 1.2e-1, "dv": 1e-1, "dbeta": 5.5e-1, "dg": 4e-1,
              "dh0": 1.1e-1},
 }
 OUTS_FWD = ("o", "hT")
